@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark: verified draft positions per second on one MI355X.
+
+A step is one verify round of the whole path on one batch of synthetic input:
+confidence truncation (when the workload truncates), LM-head logits with row
+statistics, then greedy or rejection-sampling acceptance with the correction
+or bonus token. Inputs are staged in HBM before timing; the timed steps run
+as one HIP-graph replay. Verified positions are counted on the GPU (the
+drafts-verified counter, sum over requests of L_r).
+
+Default workload: greedy verify of a 9-token block, B=1, d=2048, V=32768,
+1000 seeded steps. The LM head (134 MB) would otherwise stay resident in the
+256 MB last-level cache between steps; three copies are rotated so every
+step streams it from HBM, as it would behind a real model's layers.
+
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="greedy-block9")
+    ap.add_argument("--distinct", type=int, default=None,
+                    help="distinct pre-staged steps cycled through (default: all for the "
+                         "greedy block workload, 8 otherwise)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly, no HIP graph")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="time only the LM-head verify call (for profiler runs)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["sd_gemm.hip", "sd_accept.hip", "sd_internal.h"]:
+        with open(os.path.join(ROOT, "draft_block_verification_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the verify path is measured on one GPU's full-vocabulary share).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import draft_block_verification_amd as sd
+    from synth import make_step, make_weights, workload
+
+    w = workload(args.workload)
+    K = args.steps if args.steps is not None else (1000 if w.name == "greedy-block9" else 50)
+    Wu = args.warmup
+    S = args.distinct or (w.steps if w.name in ("greedy-block9", "tiny-greedy") else 8)
+    S = max(1, min(S, w.steps))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- stage inputs in HBM
+    W = make_weights(w)
+    w_bytes = W.nbytes
+    n_copies = max(1, math.ceil(2 * MALL_BYTES / w_bytes)) if w_bytes < MALL_BYTES else 1
+    W_dev = [bf16_dev(W) for _ in range(n_copies)]
+    steps_host = [make_step(w, W, i) for i in range(S)]
+    staged = []
+    for s in steps_host:
+        staged.append(dict(
+            hidden=bf16_dev(s.hidden),
+            draft_tokens=torch.from_numpy(s.draft_tokens).to(dev),
+            conf=None if s.conf is None else torch.from_numpy(s.conf).to(dev),
+            draft_logits=None if s.draft_logits is None else bf16_dev(s.draft_logits),
+            u_accept=torch.from_numpy(s.u_accept).to(dev),
+            u_resample=torch.from_numpy(s.u_resample).to(dev)))
+    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step(i):
+        st = staged[i % S]
+        vr.run(st["hidden"], W_dev[i % n_copies], st["draft_tokens"], st["conf"],
+               st["draft_logits"], st["u_accept"], st["u_resample"])
+
+    def verify_only(i):
+        st = staged[i % S]
+        sd.sd_verify_logits(st["hidden"], W_dev[i % n_copies], st["draft_tokens"],
+                            vr.verify_len, vr.row_offsets, w.T, vr.logits, vr.stats, vr.ws_verify)
+
+    def timed(fn, n, warm):
+        """Run fn(i) for n steps after `warm` untimed ones; returns milliseconds."""
+        with torch.cuda.stream(stream):
+            for i in range(warm):
+                fn(i)
+        torch.cuda.synchronize()
+        graph = None
+        if not args.eager:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(n):
+                    fn(warm + i)
+            torch.cuda.synchronize()
+        vr.counters.zero_()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(n):
+                    fn(warm + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # ---- whole-path timing
+    if args.kernel_only:
+        ms_total = timed(verify_only, K, Wu)
+        positions = None
+    else:
+        ms_total = timed(step, K, Wu)
+        positions = int(vr.counters[0].item())
+    # Rows per step from the same staged inputs (a truncation pass per distinct step).
+    rows = []
+    for i in range(S):
+        st = staged[i]
+        if w.truncate:
+            vl, _ = sd.sd_truncate_by_confidence(st["conf"], w.threshold)
+            rows.append(int(vl.sum().item()) + w.B)
+        else:
+            rows.append(w.B * (w.gamma + 1))
+    torch.cuda.synchronize()
+    mean_rows = float(np.mean([rows[i % S] for i in range(Wu, Wu + K)]))
+    if positions is None:
+        positions = int(round((mean_rows - w.B) * K))
+
+    # ---- dominant kernel: the LM-head verify call, timed alone
+    ms_verify = timed(verify_only, K, Wu) / K
+    v_bytes = w.V * w.d * 2 + mean_rows * w.d * 2 + mean_rows * 32
+    v_flops = 2.0 * mean_rows * w.V * w.d
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if v_flops / v_bytes > ridge:
+        roof = {"bound": "mfma", "achieved": v_flops / (ms_verify * 1e-3) / 1e12,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": v_bytes / (ms_verify * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    tr_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tr_path):
+        tr = json.load(open(tr_path))
+        ent = tr.get(w.name)
+        if ent and ent.get("kernel_hash") == kernel_source_hash():
+            roof["traffic"] = ent["bytes_per_launch"]
+    roof["kernel"] = "sd_verify_logits"
+    roof["avg_launch_us"] = ms_verify * 1e3
+
+    ms_step = ms_total / K
+    value = positions / (ms_total * 1e-3)
+
+    # ---- CPU oracle baseline on a bounded sample of the same steps
+    cpu = None
+    if args.cpu_seconds > 0:
+        from threadpoolctl import threadpool_info
+        from oracle import sd_oracle as O
+        W64 = O.lm_head_f64(W)
+        done_pos, t_cpu, n_cpu = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds and n_cpu < 10 * S:
+            s = steps_host[n_cpu % S]
+            t0 = time.perf_counter()
+            res = O.verify_step(s.hidden, W64, s.draft_tokens, w.T,
+                                conf=s.conf if w.truncate else None, threshold=w.threshold,
+                                draft_logit_bits=s.draft_logits, u_accept=s.u_accept,
+                                u_resample=s.u_resample)
+            t_cpu += time.perf_counter() - t0
+            done_pos += int(res.accept.counters[0])
+            n_cpu += 1
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        cpu = {"value": done_pos / t_cpu, "unit": "verified draft positions/s",
+               "cores": int(max(blas) if blas else 1), "kind": "oracle",
+               "sample": f"{n_cpu} steps of {w.name} (fp64 numpy oracle, inputs pre-generated)"}
+
+    out = {
+        "metric": "verified draft positions/sec at 1 GPU; % HBM or MFMA roofline",
+        "value": value,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "gamma": w.gamma, "d": w.d, "V": w.V,
+                   "temperature": w.T, "truncate": w.truncate, "distinct_steps": S,
+                   "lm_head_copies": n_copies, "mean_rows": mean_rows,
+                   "launch": "eager" if args.eager else "hipgraph",
+                   "timed": "verify only" if args.kernel_only else "truncate+verify+accept"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

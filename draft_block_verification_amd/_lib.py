@@ -1,0 +1,280 @@
+"""ctypes binding of libsdverify.so: argument marshalling only.
+
+Every step of the verify path runs in the library's HIP kernels; this module
+checks tensor dtypes, devices and shapes, allocates outputs with torch when
+the caller does not pass them, and forwards raw device pointers plus the
+current HIP stream. There is no fallback: if the shared library is missing,
+importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsdverify.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+_SIGS = {
+    "sd_abi_version": (_i32, []),
+    "sd_status_string": (ctypes.c_char_p, [_i32]),
+    "sd_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "sd_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "sd_workspace_init": (_i32, [_vp, _sz, _vp]),
+    "sd_device_flags": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32), _i32]),
+    "sd_truncate_by_confidence": (_i32, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "sd_verify_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "sd_accept_greedy": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "sd_accept_rejection": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32,
+                                   _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+# Layout of sd_row_stats (32 bytes).
+ROW_STATS_DTYPE = np.dtype([("argmax", "<i4"), ("top1", "<f4"), ("top2", "<f4"), ("pos", "<i4"),
+                            ("lse", "<f8"), ("z_draft", "<f8")])
+assert ROW_STATS_DTYPE.itemsize == 32
+
+FLAG_VERIFY_LEN, FLAG_ROW_OFFSETS, FLAG_NO_RESIDUAL = 1, 2, 4
+
+
+class SdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_lib.sd_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SdError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def abi_version() -> int:
+    return int(_lib.sd_abi_version())
+
+
+def verify_workspace_bytes(B: int, gamma: int, d: int, V: int) -> int:
+    return int(_lib.sd_verify_workspace_bytes(B, gamma, d, V))
+
+
+def accept_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return int(_lib.sd_accept_workspace_bytes(B, gamma, V))
+
+
+def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    _check("sd_workspace_init", _lib.sd_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def device_flags(workspace: torch.Tensor, clear: bool = True, stream=None) -> int:
+    out = ctypes.c_uint32(0)
+    _check("sd_device_flags", _lib.sd_device_flags(_ptr(workspace), _stream(stream),
+                                                   ctypes.byref(out), int(clear)))
+    return int(out.value)
+
+
+def new_stats(B: int, gamma: int, device) -> torch.Tensor:
+    """Device buffer for B * (gamma + 1) sd_row_stats records (viewed as int64 [rows][4])."""
+    return torch.empty((B * (gamma + 1), 4), dtype=torch.int64, device=device)
+
+
+def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:
+    """Host copy of a stats buffer as a structured array with the sd_row_stats fields."""
+    return stats.detach().cpu().numpy().view(ROW_STATS_DTYPE).reshape(-1)
+
+
+# ------------------------------------------------------------------ entry points
+
+def sd_truncate_by_confidence(conf: torch.Tensor, threshold: float,
+                              verify_len: Optional[torch.Tensor] = None,
+                              row_offsets: Optional[torch.Tensor] = None, stream=None):
+    _need(conf, "conf", torch.float32)
+    B, g = conf.shape
+    if verify_len is None:
+        verify_len = torch.empty(B, dtype=torch.int32, device=conf.device)
+    if row_offsets is None:
+        row_offsets = torch.empty(B + 1, dtype=torch.int32, device=conf.device)
+    _need(verify_len, "verify_len", torch.int32, (B,))
+    _need(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    _check("sd_truncate_by_confidence",
+           _lib.sd_truncate_by_confidence(_ptr(conf), B, g, float(threshold), _ptr(verify_len),
+                                          _ptr(row_offsets), _stream(stream)))
+    return verify_len, row_offsets
+
+
+def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
+                     draft_tokens: Optional[torch.Tensor] = None,
+                     verify_len: Optional[torch.Tensor] = None,
+                     row_offsets: Optional[torch.Tensor] = None, temperature: float = 0.0,
+                     logits: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (logits or None, stats). Pass logits=True to have one allocated."""
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(lm_head, "lm_head", torch.bfloat16)
+    B, g1, d = hidden.shape
+    g = g1 - 1
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != d:
+        raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+    dev = hidden.device
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
+    if verify_len is not None:
+        _need(verify_len, "verify_len", torch.int32, (B,))
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    if logits is True:
+        logits = torch.empty((B * g1, V), dtype=torch.float32, device=dev)
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (B * g1, V))
+    if stats is None:
+        stats = new_stats(B, g, dev)
+    _need(stats, "stats", torch.int64, (B * g1, 4))
+    if workspace is None:
+        workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
+    _check("sd_verify_logits",
+           _lib.sd_verify_logits(_ptr(hidden), _ptr(lm_head), _ptr(draft_tokens), _ptr(verify_len),
+                                 _ptr(row_offsets), B, g, d, V, float(temperature), _ptr(logits),
+                                 _ptr(stats), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return logits, stats
+
+
+def sd_accept_greedy(stats: torch.Tensor, draft_tokens: torch.Tensor,
+                     verify_len: Optional[torch.Tensor] = None,
+                     row_offsets: Optional[torch.Tensor] = None,
+                     accept_len: Optional[torch.Tensor] = None,
+                     next_token: Optional[torch.Tensor] = None,
+                     counters: Optional[torch.Tensor] = None, stream=None):
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    B, g = draft_tokens.shape
+    dev = draft_tokens.device
+    _need(stats, "stats", torch.int64, (B * (g + 1), 4))
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _need(next_token, "next_token", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    _check("sd_accept_greedy",
+           _lib.sd_accept_greedy(_ptr(stats), _ptr(draft_tokens), _ptr(verify_len),
+                                 _ptr(row_offsets), B, g, _ptr(accept_len), _ptr(next_token),
+                                 _ptr(counters), _stream(stream)))
+    return accept_len, next_token
+
+
+def sd_accept_rejection(logits: torch.Tensor, stats: torch.Tensor, draft_logits: torch.Tensor,
+                        draft_tokens: torch.Tensor, verify_len: Optional[torch.Tensor],
+                        row_offsets: Optional[torch.Tensor], u_accept: torch.Tensor,
+                        u_resample: torch.Tensor, temperature: float,
+                        accept_len: Optional[torch.Tensor] = None,
+                        next_token: Optional[torch.Tensor] = None,
+                        counters: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    B, g = draft_tokens.shape
+    dev = draft_tokens.device
+    _need(draft_logits, "draft_logits", torch.bfloat16)
+    V = draft_logits.shape[2]
+    _need(draft_logits, "draft_logits", torch.bfloat16, (B, g, V))
+    _need(logits, "logits", torch.float32, (B * (g + 1), V))
+    _need(stats, "stats", torch.int64, (B * (g + 1), 4))
+    _need(u_accept, "u_accept", torch.float32, (B, g))
+    _need(u_resample, "u_resample", torch.float32, (B, g + 1))
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    if workspace is None:
+        workspace = new_workspace(accept_workspace_bytes(B, g, V), dev, stream)
+    _check("sd_accept_rejection",
+           _lib.sd_accept_rejection(_ptr(logits), _ptr(stats), _ptr(draft_logits),
+                                    _ptr(draft_tokens), _ptr(verify_len), _ptr(row_offsets),
+                                    _ptr(u_accept), _ptr(u_resample), B, g, V, float(temperature),
+                                    _ptr(accept_len), _ptr(next_token), _ptr(counters),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return accept_len, next_token
+
+
+# --------------------------------------------------------------- a whole round
+
+class VerifyRound:
+    """Buffers for repeated verify rounds of one shape; each run() enqueues the whole path.
+
+    truncate -> verify logits -> accept (greedy when temperature == 0, else rejection),
+    all on one stream with no host synchronisation.
+    """
+
+    def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
+                 truncate: bool, threshold: float = 0.3, device="cuda", stream=None):
+        self.B, self.gamma, self.d, self.V = B, gamma, d, V
+        self.T, self.truncate, self.threshold = float(temperature), truncate, float(threshold)
+        dev = torch.device(device)
+        rows = B * (gamma + 1)
+        self.verify_len = torch.empty(B, dtype=torch.int32, device=dev) if truncate else None
+        self.row_offsets = torch.empty(B + 1, dtype=torch.int32, device=dev) if truncate else None
+        self.stats = new_stats(B, gamma, dev)
+        self.logits = (torch.empty((rows, V), dtype=torch.float32, device=dev)
+                       if self.T > 0 else None)
+        self.accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.next_token = torch.empty(B, dtype=torch.int32, device=dev)
+        self.counters = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.ws_verify = new_workspace(verify_workspace_bytes(B, gamma, d, V), dev, stream)
+        self.ws_accept = (new_workspace(accept_workspace_bytes(B, gamma, V), dev, stream)
+                          if self.T > 0 else None)
+
+    def run(self, hidden, lm_head, draft_tokens, conf=None, draft_logits=None, u_accept=None,
+            u_resample=None, stream=None):
+        if self.truncate:
+            sd_truncate_by_confidence(conf, self.threshold, self.verify_len, self.row_offsets,
+                                      stream=stream)
+        sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
+                         self.T, self.logits, self.stats, self.ws_verify, stream=stream)
+        if self.T > 0:
+            sd_accept_rejection(self.logits, self.stats, draft_logits, draft_tokens,
+                                self.verify_len, self.row_offsets, u_accept, u_resample, self.T,
+                                self.accept_len, self.next_token, self.counters, self.ws_accept,
+                                stream=stream)
+        else:
+            sd_accept_greedy(self.stats, draft_tokens, self.verify_len, self.row_offsets,
+                             self.accept_len, self.next_token, self.counters, stream=stream)
+        return self.accept_len, self.next_token

@@ -1,0 +1,190 @@
+// C ABI of libsdverify: argument validation, workspace layout and kernel dispatch.
+// Every check that can be made on the host runs before any GPU work is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "sd_internal.h"
+
+using namespace sdv;
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int kMaxGamma = 64;        // one wavefront of draft positions per request
+constexpr int kMaxVocab = 1 << 21;   // bound of the sampler's per-row tile table
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_sizes(int32_t B, int32_t gamma, int32_t d, int32_t V) {
+  if (B < 1 || gamma < 1 || gamma > kMaxGamma || d < 8 || (d % 8) != 0 || V < 1 ||
+      V > kMaxVocab)
+    return SD_ESHAPE;
+  // Row capacity, logits and partial arrays must stay addressable.
+  const int64_t cap = (int64_t)B * (gamma + 1);
+  if (cap > (int64_t)1 << 30 || cap * (int64_t)V > ((int64_t)1 << 46) ||
+      (int64_t)V * d > ((int64_t)1 << 46))
+    return SD_ESHAPE;
+  return SD_OK;
+}
+
+size_t verify_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
+  const size_t cap = (size_t)B * (gamma + 1);
+  const size_t nvt = (size_t)(V + kMinVocabTile - 1) / kMinVocabTile;
+  return sizeof(WsHeader) + align_up(cap * nvt * sizeof(TilePartial), 256);
+}
+
+size_t accept_ws_bytes(int32_t B, int32_t gamma) {
+  return sizeof(WsHeader) + align_up((size_t)B * gamma * sizeof(double), 256);
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? SD_OK : SD_EDEVICE; }
+
+// Clears n 32-bit words with a kernel (no memset node, so it is safe under graph capture).
+__global__ void k_clear_words(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t clear_words(void *p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_words, dim3((n + 63) / 64), dim3(64), 0, s,
+                     reinterpret_cast<uint32_t *>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sd_abi_version(void) { return kAbiVersion; }
+
+const char *sd_status_string(int32_t status) {
+  switch (status) {
+    case SD_OK: return "ok";
+    case SD_EINVAL: return "invalid argument (null pointer, temperature or threshold)";
+    case SD_ESHAPE: return "invalid sizes (B, gamma, d or V)";
+    case SD_EALIGN: return "misaligned tensor pointer";
+    case SD_EWORKSPACE: return "workspace missing or too small";
+    case SD_EDEVICE: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sd_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t d, int32_t V) {
+  if (check_sizes(B, gamma, d, V) != SD_OK) return 0;
+  return verify_ws_bytes(B, gamma, V);
+}
+
+size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
+  if (check_sizes(B, gamma, 8, V) != SD_OK) return 0;
+  return accept_ws_bytes(B, gamma);
+}
+
+int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+  if (!workspace || workspace_bytes < sizeof(WsHeader)) return SD_EWORKSPACE;
+  if (!aligned(workspace, 256)) return SD_EALIGN;
+  return launch_status(clear_words(workspace, sizeof(WsHeader) / 4, (hipStream_t)stream));
+}
+
+int32_t sd_device_flags(void *workspace, void *stream, uint32_t *flags, int32_t clear) {
+  if (!workspace || !flags) return SD_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return SD_EDEVICE;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SD_EDEVICE;
+  *flags = v;
+  if (clear) {
+    if (clear_words(workspace, 1, s) != hipSuccess) return SD_EDEVICE;
+    if (hipStreamSynchronize(s) != hipSuccess) return SD_EDEVICE;
+  }
+  return SD_OK;
+}
+
+int32_t sd_truncate_by_confidence(const float *conf, int32_t B, int32_t gamma, float threshold,
+                                  int32_t *verify_len, int32_t *row_offsets, void *stream) {
+  if (!conf || !verify_len || !row_offsets) return SD_EINVAL;
+  if (!isfinite(threshold)) return SD_EINVAL;
+  if (check_sizes(B, gamma, 8, 1) != SD_OK) return SD_ESHAPE;
+  if (!aligned(conf, 4) || !aligned(verify_len, 4) || !aligned(row_offsets, 4)) return SD_EALIGN;
+  return launch_status(launch_truncate(conf, B, gamma, threshold, verify_len, row_offsets,
+                                       (hipStream_t)stream));
+}
+
+int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
+                         const int32_t *draft_tokens, const int32_t *verify_len,
+                         const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                         int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  if (!hidden || !lm_head || !stats) return SD_EINVAL;
+  if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
+  if (!isfinite(temperature) || temperature < 0.f) return SD_EINVAL;
+  const int32_t sz = check_sizes(B, gamma, d, V);
+  if (sz != SD_OK) return sz;
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || !aligned(stats, 8) ||
+      (logits && !aligned(logits, 16)) || (draft_tokens && !aligned(draft_tokens, 4)) ||
+      (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
+    return SD_EALIGN;
+  if (!workspace || workspace_bytes < verify_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
+  if (!aligned(workspace, 256)) return SD_EALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  WsHeader *ws = reinterpret_cast<WsHeader *>(workspace);
+  TilePartial *partials = reinterpret_cast<TilePartial *>(reinterpret_cast<char *>(workspace) +
+                                                          sizeof(WsHeader));
+  const int n_vtiles_cap = (V + kMinVocabTile - 1) / kMinVocabTile;
+  RowMap rm{row_offsets, B, gamma};
+  int n_vtiles = 0;
+  hipError_t e = launch_verify_gemm(hidden, lm_head, rm, d, V, temperature, logits, partials,
+                                    n_vtiles_cap, ws, &n_vtiles, s);
+  if (e != hipSuccess) return SD_EDEVICE;
+  e = launch_row_merge(partials, n_vtiles, n_vtiles_cap, hidden, lm_head, draft_tokens,
+                       verify_len, rm, d, V, temperature, stats, ws, s);
+  return launch_status(e);
+}
+
+int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
+                         const int32_t *verify_len, const int32_t *row_offsets, int32_t B,
+                         int32_t gamma, int32_t *accept_len, int32_t *next_token,
+                         int64_t *counters, void *stream) {
+  if (!stats || !draft_tokens || !accept_len || !next_token) return SD_EINVAL;
+  if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
+  if (check_sizes(B, gamma, 8, 1) != SD_OK) return SD_ESHAPE;
+  if (!aligned(stats, 8) || !aligned(draft_tokens, 4) || !aligned(accept_len, 4) ||
+      !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
+    return SD_EALIGN;
+  RowMap rm{row_offsets, B, gamma};
+  return launch_status(launch_accept_greedy(stats, draft_tokens, verify_len, rm, accept_len,
+                                            next_token, counters, (hipStream_t)stream));
+}
+
+int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
+                            const uint16_t *draft_logits, const int32_t *draft_tokens,
+                            const int32_t *verify_len, const int32_t *row_offsets,
+                            const float *u_accept, const float *u_resample, int32_t B,
+                            int32_t gamma, int32_t V, float temperature, int32_t *accept_len,
+                            int32_t *next_token, int64_t *counters, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!logits || !stats || !draft_logits || !draft_tokens || !u_accept || !u_resample ||
+      !accept_len || !next_token)
+    return SD_EINVAL;
+  if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
+  if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
+  if (check_sizes(B, gamma, 8, V) != SD_OK) return SD_ESHAPE;
+  if (!aligned(logits, 16) || !aligned(stats, 8) || !aligned(draft_logits, 16) ||
+      !aligned(draft_tokens, 4) || !aligned(u_accept, 4) || !aligned(u_resample, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
+    return SD_EALIGN;
+  if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma)) return SD_EWORKSPACE;
+  if (!aligned(workspace, 256)) return SD_EALIGN;
+  WsHeader *ws = reinterpret_cast<WsHeader *>(workspace);
+  double *lse_q = reinterpret_cast<double *>(reinterpret_cast<char *>(workspace) +
+                                             sizeof(WsHeader));
+  RowMap rm{row_offsets, B, gamma};
+  return launch_status(launch_accept_rejection(logits, stats, draft_logits, draft_tokens,
+                                               verify_len, rm, u_accept, u_resample, V,
+                                               temperature, accept_len, next_token, counters,
+                                               lse_q, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations shared by the HIP translation units of libsdverify.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sd_verify.h"
+
+namespace sdv {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Workspace header: a 256-byte block at the start of every workspace.
+struct WsHeader {
+  uint32_t flags;      // sticky SD_FLAG_* bits
+  uint32_t ticket;     // arrival counter for last-workgroup epilogues (returns to 0)
+  uint32_t pad[62];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+// Statistics of one verified row over one vocabulary tile.
+struct TilePartial {
+  float top1;   // max z over the tile
+  float top2;   // max z over the tile excluding the argmax position
+  int32_t arg;  // lowest vocabulary id attaining top1
+  float sum;    // sum over the tile of exp((z - top1) / T); 0 when T == 0
+};
+static_assert(sizeof(TilePartial) == 16, "partials are 16 bytes");
+
+// Smallest vocabulary tile used by any GEMM variant; sizes the partials array.
+constexpr int kMinVocabTile = 64;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Rows of the verify problem: request r owns rows row_offsets[r] .. + L_r.
+struct RowMap {
+  const int32_t *row_offsets;  // [B + 1] or null (then rows are r * (gamma + 1) + j)
+  int32_t B;
+  int32_t gamma;
+};
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Number of verified rows, clamped to the row capacity B * (gamma + 1).
+__device__ inline int rows_total(const RowMap &rm) {
+  const int cap = rm.B * (rm.gamma + 1);
+  if (!rm.row_offsets) return cap;
+  int M = rm.row_offsets[rm.B];
+  return M < 0 ? 0 : (M > cap ? cap : M);
+}
+
+// Request owning row m: the largest r with row_offsets[r] <= m.
+__device__ inline int row_request(const RowMap &rm, int m) {
+  if (!rm.row_offsets) return m / (rm.gamma + 1);
+  int lo = 0, hi = rm.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rm.row_offsets[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Row index into hidden[B][gamma + 1] for packed row m, or -1 if the offsets are inconsistent.
+__device__ inline int hidden_row(const RowMap &rm, int m, int *req, int *pos) {
+  const int r = row_request(rm, m);
+  const int j = rm.row_offsets ? m - rm.row_offsets[r] : m - r * (rm.gamma + 1);
+  *req = r;
+  *pos = j;
+  if (j < 0 || j > rm.gamma) return -1;
+  return r * (rm.gamma + 1) + j;
+}
+
+__device__ inline void raise_flag(WsHeader *ws, uint32_t bit) {
+  if (ws) atomicOr(&ws->flags, bit);
+}
+
+// Order used for argmax: larger value first, then lower index.
+__device__ inline bool beats(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
+hipError_t launch_verify_gemm(const uint16_t *hidden, const uint16_t *W, const RowMap &rm, int d,
+                              int V, float temperature, float *logits, TilePartial *partials,
+                              int n_vtiles_cap, WsHeader *ws, int *n_vtiles_used,
+                              hipStream_t stream);
+int verify_gemm_vocab_tile(int max_rows);
+
+hipError_t launch_row_merge(const TilePartial *partials, int n_vtiles, int n_vtiles_cap,
+                            const uint16_t *hidden, const uint16_t *W,
+                            const int32_t *draft_tokens, const int32_t *verify_len,
+                            const RowMap &rm, int d, int V, float temperature,
+                            sd_row_stats *stats, WsHeader *ws, hipStream_t stream);
+
+hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
+                           int32_t *verify_len, int32_t *row_offsets, hipStream_t stream);
+
+hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
+                                const int32_t *verify_len, const RowMap &rm,
+                                int32_t *accept_len, int32_t *next_token, int64_t *counters,
+                                hipStream_t stream);
+
+hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
+                                   const uint16_t *draft_logits, const int32_t *draft_tokens,
+                                   const int32_t *verify_len, const RowMap &rm,
+                                   const float *u_accept, const float *u_resample, int V,
+                                   float temperature, int32_t *accept_len, int32_t *next_token,
+                                   int64_t *counters, double *lse_q, WsHeader *ws,
+                                   hipStream_t stream);
+
+}  // namespace sdv

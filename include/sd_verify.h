@@ -1,0 +1,193 @@
+/*
+ * sd_verify.h -- C ABI of the draft-block verification library (libsdverify.so).
+ *
+ * One verify round of speculative decoding on an AMD MI355X (gfx950):
+ *   1. sd_truncate_by_confidence  keep each request's confident draft prefix
+ *   2. sd_verify_logits           LM-head logits at every kept position plus the
+ *                                 bonus position, with per-row statistics
+ *   3. sd_accept_greedy           greedy prefix acceptance + correction/bonus token
+ *      sd_accept_rejection        rejection-sampling acceptance + residual/bonus draw
+ *
+ * Conventions shared by every call
+ *   - All tensors are row-major, contiguous, caller-owned DEVICE memory unless
+ *     stated otherwise. The library never allocates; scratch memory comes from a
+ *     caller-provided workspace sized by the *_workspace_bytes functions.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work; outputs are valid once the stream has been synchronised.
+ *   - Host-checkable errors (null pointers, bad sizes, misalignment, small
+ *     workspace) are returned synchronously before any GPU work is enqueued.
+ *     SD_EDEVICE reports a failed kernel launch. Nothing is printed.
+ *   - Device-side anomalies (a verify length outside [0, gamma], row offsets
+ *     that disagree with the lengths, a residual with no positive mass) are
+ *     clamped or handled by a documented fallback and raise bits in a sticky
+ *     flag word inside the workspace, read with sd_device_flags.
+ *   - Identical inputs give identical output bytes (fixed-order reductions, no
+ *     floating-point atomics).
+ *   - Rows: request r verifies L_r kept drafts (0 <= L_r <= gamma) plus one bonus
+ *     row, M = sum_r (L_r + 1) rows in total, packed with no padding. Row m of
+ *     request r, block position j (0 <= j <= L_r) is m = row_offsets[r] + j and
+ *     reads hidden[r][j][:]. Per-row outputs have capacity B * (gamma + 1) rows;
+ *     only the first M are written.
+ *
+ * The operations follow these passages:
+ *   DSpark summary (GeekNews), "Problem definition": the target checks a drafted
+ *     block in one forward pass and rejection sampling accepts the longest
+ *     prefix consistent with the target distribution, losslessly.
+ *   DSpark summary, "Architecture" (decode-round example, confidence head,
+ *     prefix scheduler): per-position survival confidences; the scheduler keeps
+ *     the confident prefix and cuts the rest; on the first rejection the target
+ *     emits a correction token.
+ *   DSpark summary, "Production deployment": the LM head maps the d-dimensional
+ *     hidden state to V logits; variable-length requests are flattened into
+ *     independent elements instead of padded.
+ *   LFM2.5-DSpark blog, "How DSpark works" and "Quality parity": verification
+ *     shares one weight load across the block; in greedy decoding a draft is
+ *     kept only if it matches the target and is otherwise replaced by the
+ *     target's token, so the output equals the target's own greedy output.
+ */
+#ifndef SD_VERIFY_H
+#define SD_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef SD_API
+#define SD_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point (as int32_t). */
+enum {
+    SD_OK = 0,
+    SD_EINVAL = 1,      /* null required pointer, bad temperature or threshold   */
+    SD_ESHAPE = 2,      /* B < 1, gamma outside [1, 64], d % 8 != 0, V < 1, size overflow */
+    SD_EALIGN = 3,      /* a bf16 / fp32 tensor not 16-byte aligned, stats not 8-byte aligned */
+    SD_EWORKSPACE = 4,  /* workspace pointer null or smaller than required       */
+    SD_EDEVICE = 5      /* a HIP launch or copy failed                           */
+};
+
+/* Sticky device flags (bit mask) accumulated in a workspace. */
+enum {
+    SD_FLAG_VERIFY_LEN = 1,   /* a verify_len entry was outside [0, gamma] and was clamped */
+    SD_FLAG_ROW_OFFSETS = 2,  /* row_offsets disagreed with verify_len or overflowed the row capacity */
+    SD_FLAG_NO_RESIDUAL = 4   /* a residual max(0, p - q) had no positive mass; drew from p instead */
+};
+
+/* Per verified row statistics (32 bytes, 8-byte aligned). */
+typedef struct sd_row_stats {
+    int32_t argmax;   /* lowest vocabulary id attaining max_v z[v]                        */
+    float top1;       /* z[argmax] (fp32 logit)                                          */
+    float top2;       /* largest z[v] over v != argmax (equals top1 on an exact tie)      */
+    int32_t pos;      /* block position j of this row (0..L_r; L_r is the bonus row)      */
+    double lse;       /* log sum_v exp(z[v] / T) when T > 0, else 0                      */
+    double z_draft;   /* logit of the drafted token x[r][j] for j < L_r, as an fp64 dot of
+                         the bf16 inputs; 0 on the bonus row                              */
+} sd_row_stats;
+
+/* ABI version of this header (incremented on any signature or layout change). */
+SD_API int32_t sd_abi_version(void);
+
+/* Static text for a status code. */
+SD_API const char *sd_status_string(int32_t status);
+
+/* Workspace bytes sd_verify_logits needs for these sizes (0 on invalid sizes). */
+SD_API size_t sd_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t d, int32_t V);
+
+/* Workspace bytes sd_accept_rejection needs for these sizes (0 on invalid sizes). */
+SD_API size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
+
+/* Prepare a freshly allocated workspace (clears its flag word and counters).
+ * Must be called once per workspace before its first use; enqueued on `stream`. */
+SD_API int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Synchronise `stream`, copy the sticky flag word of `workspace` to *flags (host) and,
+ * if clear != 0, reset it to zero. */
+SD_API int32_t sd_device_flags(void *workspace, void *stream, uint32_t *flags, int32_t clear);
+
+/*
+ * Confidence truncation (DSpark summary, "Architecture": the scheduler keeps
+ * the confident prefix E F G and cuts the low-confidence H).
+ *   conf        fp32 [B][gamma]  per-position prefix-survival confidences
+ *   threshold   keep leading positions with conf >= threshold (finite, any value)
+ *   verify_len  int32 [B]        out: L_r = number of leading positions kept
+ *   row_offsets int32 [B + 1]    out: exclusive prefix sum of (L_r + 1); row_offsets[B] = M
+ */
+SD_API int32_t sd_truncate_by_confidence(const float *conf, int32_t B, int32_t gamma, float threshold,
+                                  int32_t *verify_len, int32_t *row_offsets, void *stream);
+
+/*
+ * Target logits at every verified row and their statistics (LFM2.5-DSpark
+ * blog, "How DSpark works"; DSpark summary, "Production deployment").
+ *   hidden       bf16 [B][gamma + 1][d]  target hidden states before the LM head
+ *   lm_head      bf16 [V][d]             LM-head weight, d-contiguous rows
+ *   draft_tokens int32 [B][gamma] or NULL drafted tokens (for z_draft); NULL -> z_draft = 0
+ *   verify_len   int32 [B] or NULL       kept drafts per request; NULL -> gamma for all
+ *   row_offsets  int32 [B + 1] or NULL   packed row starts; NULL -> r * (gamma + 1).
+ *                                        verify_len and row_offsets are both NULL or both set.
+ *   temperature  >= 0; 0 computes argmax/top1/top2 only (lse = 0)
+ *   logits       fp32 [B * (gamma + 1)][V] or NULL: out, z[m][v] for m < M
+ *   stats        sd_row_stats [B * (gamma + 1)]: out, rows m < M
+ *   workspace    device scratch of sd_verify_workspace_bytes(B, gamma, d, V) bytes
+ * z[m][v] = sum_k hidden_row(m)[k] * lm_head[v][k], bf16 products accumulated in fp32.
+ */
+SD_API int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
+                         const int32_t *draft_tokens, const int32_t *verify_len,
+                         const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                         int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy acceptance (LFM2.5-DSpark blog, "Quality parity"): a_r = first j < L_r
+ * with stats[row_offsets[r] + j].argmax != draft_tokens[r][j], else L_r; the
+ * emitted token is the target argmax of row a_r (a correction when a_r < L_r,
+ * the bonus token otherwise).
+ *   stats        from sd_verify_logits
+ *   draft_tokens int32 [B][gamma]
+ *   verify_len, row_offsets  as for sd_verify_logits (both NULL or both set)
+ *   accept_len   int32 [B]  out: a_r
+ *   next_token   int32 [B]  out
+ *   counters     int64 [2] or NULL: counters[0] += sum_r L_r (drafts verified),
+ *                counters[1] += sum_r a_r (drafts accepted)
+ */
+SD_API int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
+                         const int32_t *verify_len, const int32_t *row_offsets, int32_t B,
+                         int32_t gamma, int32_t *accept_len, int32_t *next_token,
+                         int64_t *counters, void *stream);
+
+/*
+ * Rejection-sampling acceptance (DSpark summary, "Problem definition":
+ * lossless acceptance of the longest consistent prefix; "Architecture":
+ * correction token on the first rejection). With p_j = softmax(z_j / T) and
+ * q_j = softmax(draft_logits[r][j] / T):
+ *   position j < L_r survives iff u_accept[r][j] < min(1, p_j(x_j) / q_j(x_j));
+ *   a_r = first failing j, else L_r;
+ *   if a_r < L_r the token is drawn from norm(max(0, p_a - q_a)), else from p_{L_r};
+ *   draws are inverse-CDF in ascending vocabulary id: the smallest v whose running
+ *   weight exceeds u_resample[r][a_r] times the total weight.
+ *   logits       fp32 [B * (gamma + 1)][V] written by sd_verify_logits
+ *   stats        from sd_verify_logits at the same temperature
+ *   draft_logits bf16 [B][gamma][V]     drafter logits per block position
+ *   draft_tokens int32 [B][gamma]
+ *   u_accept     fp32 [B][gamma]        uniforms in [0, 1)
+ *   u_resample   fp32 [B][gamma + 1]    uniforms in [0, 1), indexed by the row sampled
+ *   temperature  > 0 (the same one given to sd_verify_logits)
+ *   accept_len, next_token, counters   as for sd_accept_greedy
+ *   workspace    device scratch of sd_accept_workspace_bytes(B, gamma, V) bytes
+ */
+SD_API int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
+                            const uint16_t *draft_logits, const int32_t *draft_tokens,
+                            const int32_t *verify_len, const int32_t *row_offsets,
+                            const float *u_accept, const float *u_resample, int32_t B,
+                            int32_t gamma, int32_t V, float temperature, int32_t *accept_len,
+                            int32_t *next_token, int64_t *counters, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_VERIFY_H */

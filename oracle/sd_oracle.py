@@ -110,19 +110,23 @@ def verified_rows(hidden_bits: np.ndarray, verify_len: np.ndarray) -> np.ndarray
     return np.concatenate(rows, axis=0)
 
 
+def lm_head_f64(W_bits: np.ndarray) -> np.ndarray:
+    """The LM-head weight as float64 (bf16 bits are decoded; float64 input is returned as is)."""
+    W = np.asarray(W_bits)
+    return W if W.dtype == np.float64 else bf16_decode(W)
+
+
 def verify_logits(hidden_bits: np.ndarray, W_bits: np.ndarray,
                   verify_len: np.ndarray) -> np.ndarray:
     """Target logits z[m][v] = sum_k h[m][k] * W[v][k] at every verified row (float64)."""
     H = verified_rows(hidden_bits, verify_len)
-    W = bf16_decode(W_bits)
-    return H @ W.T
+    return H @ lm_head_f64(W_bits).T
 
 
 def logits_at(hidden_bits: np.ndarray, W_bits: np.ndarray, r: int, j: int) -> np.ndarray:
     """One target row z[v] for request r, block position j (float64); for sampled checks."""
     h = bf16_decode(hidden_bits[r, j])
-    W = bf16_decode(W_bits)
-    return W @ h
+    return lm_head_f64(W_bits) @ h
 
 
 # --------------------------------------------------------------- row stats
@@ -251,9 +255,8 @@ def accept_rejection(z: np.ndarray, draft_logit_bits: np.ndarray, draft_tokens: 
             q = np.exp(lq[j, x] - lse_q[r, j])
             p_x[r, j], q_x[r, j] = p, q
             ratio[r, j] = p / q
-            if not float(u_accept[r, j]) < min(1.0, p / q):
-                a = j
-                break
+            if a == L and not float(u_accept[r, j]) < min(1.0, p / q):
+                a = j          # first rejection; later rows only fill the diagnostics
         acc[r] = a
         p_row = np.exp(z[base + a] / T - lse_p[base + a])
         u = float(u_resample[r, a])

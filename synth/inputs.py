@@ -75,9 +75,9 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, **overrides) -> Workload:
+def workload(key: str, **overrides) -> Workload:
     """A named workload, optionally with fields replaced (smaller V, stress planting)."""
-    base = WORKLOADS[name]
+    base = WORKLOADS[key]
     return dataclasses.replace(base, **overrides) if overrides else base
 
 

@@ -1,0 +1,104 @@
+"""The C ABI on the host: exported symbols, workspace sizing, argument validation.
+
+Nothing here launches GPU work: every call below fails a host-side check
+before the library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_block_verification_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd_verify.h")
+
+lib = ctypes.CDLL(sd.LIB_PATH)
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced on the host
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^SD_API\s+[\w\s\*]*?\b(sd_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(sd.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings():
+    assert sd.abi_version() == 1
+    lib.sd_status_string.restype = ctypes.c_char_p
+    assert lib.sd_status_string(0) == b"ok"
+    assert b"workspace" in lib.sd_status_string(4)
+    assert lib.sd_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    # Header + one 16-byte partial per (row capacity, 64-wide vocabulary tile).
+    b = sd.verify_workspace_bytes(1, 9, 2048, 32768)
+    assert b == 256 + ((10 * 512 * 16 + 255) // 256) * 256
+    assert sd.verify_workspace_bytes(32, 16, 4096, 151936) >= 32 * 17 * (151936 // 64) * 16
+    assert sd.accept_workspace_bytes(128, 16, 129280) == 256 + 128 * 16 * 8
+    for bad in [(0, 9, 2048, 100), (1, 0, 2048, 100), (1, 65, 2048, 100), (1, 4, 12, 100),
+                (1, 4, 2048, 0), (1, 4, 2048, 1 << 22)]:
+        assert sd.verify_workspace_bytes(*bad) == 0, bad
+
+
+def _verify(**kw):
+    a = dict(hidden=FAKE, lm_head=FAKE, draft=None, vlen=None, offs=None, B=1, g=4, d=256,
+             V=1024, T=0.0, logits=None, stats=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.sd_verify_logits(a["hidden"], a["lm_head"], a["draft"], a["vlen"], a["offs"],
+                                ctypes.c_int32(a["B"]), ctypes.c_int32(a["g"]),
+                                ctypes.c_int32(a["d"]), ctypes.c_int32(a["V"]),
+                                ctypes.c_float(a["T"]), a["logits"], a["stats"], a["ws"],
+                                ctypes.c_size_t(a["ws_bytes"]), a["stream"])
+
+
+def test_verify_logits_host_validation():
+    assert _verify(hidden=None) == 1
+    assert _verify(stats=None) == 1
+    assert _verify(vlen=FAKE) == 1                    # lengths without offsets
+    assert _verify(T=-1.0) == 1
+    assert _verify(T=float("nan")) == 1
+    assert _verify(d=12) == 2
+    assert _verify(g=65) == 2
+    assert _verify(B=0) == 2
+    assert _verify(V=0) == 2
+    assert _verify(hidden=MISALIGNED) == 3
+    assert _verify(logits=MISALIGNED) == 3
+    assert _verify(ws=None) == 4
+    assert _verify(ws_bytes=100) == 4
+    assert _verify(ws=ctypes.c_void_p(0x10010)) == 3  # workspace must be 256-byte aligned
+
+
+def test_truncate_and_accept_host_validation():
+    f = lib.sd_truncate_by_confidence
+    assert f(None, 1, 4, ctypes.c_float(0.3), FAKE, FAKE, None) == 1
+    assert f(FAKE, 1, 4, ctypes.c_float(float("inf")), FAKE, FAKE, None) == 1
+    assert f(FAKE, 0, 4, ctypes.c_float(0.3), FAKE, FAKE, None) == 2
+    assert f(MISALIGNED, 1, 4, ctypes.c_float(0.3), FAKE, FAKE, None) == 3
+    g = lib.sd_accept_greedy
+    assert g(FAKE, None, None, None, 1, 4, FAKE, FAKE, None, None) == 1
+    assert g(FAKE, FAKE, FAKE, None, 1, 4, FAKE, FAKE, None, None) == 1
+    assert g(FAKE, FAKE, None, None, 1, 99, FAKE, FAKE, None, None) == 2
+    assert g(MISALIGNED, FAKE, None, None, 1, 4, FAKE, FAKE, None, None) == 3
+    r = lib.sd_accept_rejection
+    args = [FAKE] * 8 + [1, 4, 1024, ctypes.c_float(1.0)] + [FAKE, FAKE, None, FAKE,
+                                                             ctypes.c_size_t(1 << 20), None]
+    bad_T = list(args)
+    bad_T[11] = ctypes.c_float(0.0)
+    assert r(*bad_T) == 1                             # rejection needs T > 0
+    no_ws = list(args)
+    no_ws[15] = None
+    assert r(*no_ws) == 4
+    small_ws = list(args)
+    small_ws[16] = ctypes.c_size_t(64)
+    assert r(*small_ws) == 4

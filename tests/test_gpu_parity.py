@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case draws seeded inputs, runs truncate -> verify -> accept on the GPU
+and the same round in the oracle, and compares per request (see _parity for
+the bars and the exemptions). Full-size workloads that the oracle cannot
+finish in seconds are checked on sampled requests, whose rows the oracle
+computes exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import draft_block_verification_amd as sd
+from oracle import sd_oracle as O
+from synth import make_step, make_weights, workload
+
+from _parity import (Report, attach_inputs, bf16_dev, check_logits_rows, compare, run_gpu,
+                     run_oracle, slice_step, upload_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    yield
+
+
+def full_case(w, steps, seed=0, check_all_logits=True):
+    """Oracle over whole batches: every request and every logit compared."""
+    W = make_weights(w, seed)
+    W64 = O.lm_head_f64(W)
+    W_dev = bf16_dev(W)
+    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold)
+    rep = Report()
+    for st in steps:
+        say(w.name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={st} seed={seed}")
+        s = make_step(w, W, st, seed)
+        g = run_gpu(w, W_dev, upload_step(s), vr, fetch_all_logits=check_all_logits and w.T > 0)
+        o = attach_inputs(run_oracle(w, W64, s), s)
+        assert g.flags == 0, f"device flags {g.flags}"
+        compare(w, g, o, range(w.B), rep)
+        if g.logits is not None:
+            check_logits_rows(w, g.logits, o.z, rep)
+        assert np.array_equal(g.counters, o.accept.counters)
+    say("report", rep)
+    return rep
+
+
+# ---------------------------------------------------------------- small shapes
+
+SHAPES = [
+    # (name, B, gamma, d, V, T, truncate): skinny 16/32/64-row tiles, LDS-tiled
+    # path, a K tail (d % 32 != 0), vocabulary tails (V % 64 != 0, V % 8 != 0).
+    ("skinny16-greedy", 1, 4, 256, 1000, 0.0, False),
+    ("skinny16-rej", 2, 5, 40, 1001, 1.0, False),
+    ("skinny32-rej", 1, 16, 264, 3000, 0.7, False),
+    ("skinny64-trunc", 3, 16, 128, 777, 1.3, True),
+    ("tiled-greedy", 9, 9, 512, 2050, 0.0, False),
+    ("tiled-trunc-rej", 40, 16, 200, 5000, 1.0, True),
+    ("gamma64", 2, 64, 64, 300, 1.0, False),
+    ("many-requests", 300, 3, 64, 129, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=[c[0] for c in SHAPES])
+def test_small_shapes(case):
+    name, B, g, d, V, T, trunc = case
+    w = workload("ragged-b32", B=B, gamma=g, d=d, V=V, T=T, truncate=trunc,
+                 geo_p=(0.2,), name=name)
+    full_case(w, steps=range(3))
+
+
+def test_stress_long_prefixes():
+    """Planting 12 along the drafted row: long accepted prefixes exercise late positions."""
+    w = workload("rejection-b1", V=20000, d=512, plant=12.0, name="stress-rej")
+    rep = full_case(w, steps=range(6))
+    assert rep.accepted >= 6 * 4
+    w = workload("greedy-block9", V=20000, d=512, plant=12.0, geo_p=(0.05,), name="stress-greedy")
+    rep = full_case(w, steps=range(20))
+    assert rep.accepted >= 20 * 5
+
+
+def test_truncation_edge_thresholds():
+    """Threshold above every confidence (only bonus rows) and at zero (all kept)."""
+    for thr in (1.5, 0.0):
+        w = workload("ragged-b32", V=4096, d=256, threshold=thr, name=f"thr{thr}")
+        full_case(w, steps=range(2))
+
+
+# ----------------------------------------------------------- named workloads
+
+def test_workload_tiny_greedy_all_steps():
+    w = workload("tiny-greedy")
+    rep = full_case(w, steps=range(w.steps))
+    assert rep.requests == 1000
+
+
+def test_workload_greedy_block9():
+    w = workload("greedy-block9")
+    full_case(w, steps=range(100))
+
+
+def test_workload_rejection_b1():
+    w = workload("rejection-b1")
+    full_case(w, steps=range(6))
+
+
+def test_workload_ragged_b32():
+    w = workload("ragged-b32")
+    full_case(w, steps=range(2))
+
+
+def test_workload_concurrency_b128_sampled():
+    """Full size (W 1.85 GB); the oracle computes a sample of requests exactly."""
+    w = workload("concurrency-b128")
+    W = make_weights(w)
+    W_dev = bf16_dev(W)
+    W64 = O.lm_head_f64(W)
+    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold)
+    rep = Report()
+    rng = np.random.default_rng(99)
+    for st in range(2):
+        say(w.name, f"step={st} sampled")
+        s = make_step(w, W, st)
+        ds = upload_step(s)
+        g = run_gpu(w, W_dev, ds, vr)
+        assert g.flags == 0
+        req = sorted(set(rng.choice(w.B, 6, replace=False).tolist()) | {0, w.B - 1})
+        o = attach_inputs(run_oracle(w, W64, slice_step(s, req)), slice_step(s, req))
+        compare(w, g, o, req, rep)
+        rows = [int(g.row_offsets[r]) + j for r in req for j in range(int(g.verify_len[r]) + 1)]
+        idx = torch.as_tensor(rows, dtype=torch.long, device=vr.logits.device)
+        check_logits_rows(w, vr.logits.index_select(0, idx).cpu().numpy(), o.z, rep)
+        # Counters cover the whole batch: compare with the GPU's own per-request outputs.
+        assert g.counters[0] == g.verify_len.sum() and g.counters[1] == g.accept_len.sum()
+    say("report", rep)
+
+
+# --------------------------------------------------------------- properties
+
+def test_determinism_bytes():
+    w = workload("ragged-b32", V=30000, d=1024, name="determinism")
+    W = make_weights(w)
+    W_dev = bf16_dev(W)
+    ds = upload_step(make_step(w, W, 0))
+    outs = []
+    for _ in range(2):
+        vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold)
+        vr.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf, ds.draft_logits, ds.u_accept,
+               ds.u_resample)
+        torch.cuda.synchronize()
+        M = int(vr.row_offsets[-1].item())
+        outs.append([t.clone() for t in (vr.stats[:M], vr.logits[:M], vr.accept_len,
+                                         vr.next_token, vr.row_offsets)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_rejection_lossless_on_gpu():
+    """Bigram target and drafter over V = 8: emitted first tokens follow the target."""
+    from scipy import special, stats as sstats
+    rng = np.random.default_rng(77)
+    V, g, B = 8, 3, 40000
+    Zt = rng.standard_normal((V, V)).astype(np.float32)
+    Zd = rng.standard_normal((V, V)).astype(np.float32)
+    from synth import bf16_round, bf16_to_f32
+    Zt = bf16_to_f32(bf16_round(Zt)).astype(np.float64)
+    Zd = bf16_to_f32(bf16_round(Zd)).astype(np.float64)
+    qt = special.softmax(Zd, axis=1)
+    x = np.zeros((B, g), np.int32)
+    prev = np.zeros(B, np.int64)
+    for j in range(g):
+        cdf = np.cumsum(qt[prev], axis=1)
+        x[:, j] = np.minimum((rng.random((B, 1)) > cdf).sum(1), V - 1)
+        prev = x[:, j]
+    prevs = np.concatenate([np.zeros((B, 1), np.int64), x], axis=1)
+    hidden = bf16_round(Zt[prevs].astype(np.float32))
+    dl = bf16_round(Zd[prevs[:, :g]].astype(np.float32))
+    W = bf16_round(np.eye(V, dtype=np.float32))
+    say("lossless-gpu", f"B={B} V={V}")
+    vr = sd.VerifyRound(B, g, V, V, 1.0, False)
+    vr.run(bf16_dev(hidden), bf16_dev(W), torch.from_numpy(x).cuda(), None, bf16_dev(dl),
+           torch.from_numpy(rng.random((B, g)).astype(np.float32)).cuda(),
+           torch.from_numpy(rng.random((B, g + 1)).astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    a = vr.accept_len.cpu().numpy()
+    n = vr.next_token.cpu().numpy()
+    first = np.where(a > 0, x[:, 0], n)
+    pt = special.softmax(Zt, axis=1)
+    cnt = np.bincount(first, minlength=V)
+    assert sstats.chisquare(cnt, pt[0] / pt[0].sum() * B).pvalue > 1e-3
+    rate = np.mean(a >= 1)
+    want = 1 - 0.5 * np.abs(pt[0] - qt[0]).sum()
+    assert abs(rate - want) < 4 * np.sqrt(want * (1 - want) / B)
+
+
+def test_out_of_range_lengths_are_clamped_and_flagged():
+    w = workload("ragged-b32", B=4, V=2048, d=128, truncate=False, T=0.0, name="clamp")
+    W = make_weights(w)
+    s = make_step(w, W, 0)
+    bad = np.array([99, -3, 5, 16], np.int32)
+    L = np.clip(bad, 0, w.gamma)
+    offs = np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)
+    ds = upload_step(s)
+    say("clamp", bad.tolist())
+    vlen_d = torch.from_numpy(bad).cuda()
+    offs_d = torch.from_numpy(offs).cuda()
+    ws = sd.new_workspace(sd.verify_workspace_bytes(w.B, w.gamma, w.d, w.V), "cuda")
+    _, st = sd.sd_verify_logits(ds.hidden, bf16_dev(W), ds.draft_tokens, vlen_d, offs_d, 0.0,
+                                workspace=ws)
+    acc, nxt = sd.sd_accept_greedy(st, ds.draft_tokens, vlen_d, offs_d)
+    torch.cuda.synchronize()
+    assert sd.device_flags(ws) & sd.FLAG_VERIFY_LEN
+    z = O.verify_logits(s.hidden, W, L)
+    o = O.accept_greedy(np.argmax(z, axis=1), s.draft_tokens, L, offs)
+    assert np.array_equal(acc.cpu().numpy(), o.accept_len)
+    assert np.array_equal(nxt.cpu().numpy(), o.next_token)
