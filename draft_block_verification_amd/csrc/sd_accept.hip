@@ -20,16 +20,6 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
 
-__device__ inline int clamp_len(const int32_t *verify_len, int r, int gamma, WsHeader *ws) {
-  if (!verify_len) return gamma;
-  int L = verify_len[r];
-  if (L < 0 || L > gamma) {
-    raise_flag(ws, SD_FLAG_VERIFY_LEN);
-    L = L < 0 ? 0 : gamma;
-  }
-  return L;
-}
-
 // First row of request r, or -1 when rows r .. r + L would leave the row capacity.
 __device__ inline int request_base(const RowMap &rm, int r, int L, WsHeader *ws) {
   const int cap = rm.B * (rm.gamma + 1);
@@ -75,120 +65,37 @@ __global__ __launch_bounds__(256) void k_truncate(const float *__restrict__ conf
   if (tid == 255) row_offsets[B] = sums[255];
 }
 
-// ------------------------------------------------------------------ row merge
-// One wave per verified row: merge the vocabulary-tile partials into the row's
-// argmax / top-2 / log-sum-exp and take the drafted token's logit as an fp64
-// dot product of the bf16 inputs (bf16 x bf16 products are exact in fp64).
-__global__ __launch_bounds__(256) void k_row_merge(const TilePartial *__restrict__ partials,
-                                                   int n_vtiles, int n_vtiles_cap,
-                                                   const uint16_t *__restrict__ hidden,
-                                                   const uint16_t *__restrict__ W,
-                                                   const int32_t *__restrict__ draft_tokens,
-                                                   const int32_t *__restrict__ verify_len,
-                                                   RowMap rm, int d, int V, float temperature,
-                                                   sd_row_stats *__restrict__ stats, WsHeader *ws) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int M = rows_total(rm);
-  if (m >= M) return;
-  const TilePartial *P = partials + (size_t)m * n_vtiles_cap;
-
-  float t1 = -INFINITY, t2 = -INFINITY;
-  int a1 = 0x7fffffff;
-  for (int t = lane; t < n_vtiles; t += kWave) {
-    const TilePartial p = P[t];
-    if (beats(p.top1, p.arg, t1, a1)) { t2 = fmaxf(t1, p.top2); t1 = p.top1; a1 = p.arg; }
-    else { t2 = fmaxf(t2, p.top1); }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-    const int oa = __shfl_xor(a1, off);
-    if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-    else { t2 = fmaxf(t2, o1); }
-  }
-
-  double lse = 0.0;
-  if (temperature > 0.f) {
-    const double invT = 1.0 / (double)temperature;
-    double S = 0.0;
-    for (int t = lane; t < n_vtiles; t += kWave) {
-      const TilePartial p = P[t];
-      S += (double)p.sum * exp(((double)p.top1 - (double)t1) * invT);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-    lse = (double)t1 * invT + log(S);
-  }
-
-  int r, j;
-  const int hr = hidden_row(rm, m, &r, &j);
-  double zd = 0.0;
-  if (hr >= 0 && draft_tokens) {
-    const int L = clamp_len(verify_len, r, rm.gamma, ws);
-    if (j < L) {
-      const int x = draft_tokens[(size_t)r * rm.gamma + j];
-      if (x >= 0 && x < V) {
-        const uint16_t *h = hidden + (size_t)hr * d;
-        const uint16_t *w = W + (size_t)x * d;
-        for (int k = lane; k < d; k += kWave)
-          zd += (double)bf16_to_f32(h[k]) * (double)bf16_to_f32(w[k]);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) zd += __shfl_xor(zd, off);
-      }
-    }
-  }
-  if (lane == 0) {
-    sd_row_stats st;
-    st.argmax = a1;
-    st.top1 = t1;
-    st.top2 = t2;
-    st.pos = j;
-    st.lse = lse;
-    st.z_draft = zd;
-    stats[m] = st;
-  }
-}
-
 // -------------------------------------------------------------- greedy accept
+// One wave per request: lane j compares row j's argmax with draft j, a ballot finds
+// the first mismatch, and the emitted token is the argmax of that row.
 __global__ __launch_bounds__(256) void k_accept_greedy(const sd_row_stats *__restrict__ stats,
                                                        const int32_t *__restrict__ draft_tokens,
                                                        const int32_t *__restrict__ verify_len,
                                                        RowMap rm, int32_t *__restrict__ accept_len,
                                                        int32_t *__restrict__ next_token,
                                                        int64_t *__restrict__ counters) {
-  __shared__ long long red[2][256];
-  const int tid = threadIdx.x;
-  long long sumL = 0, sumA = 0;
-  for (int r = tid; r < rm.B; r += 256) {
-    const int L = clamp_len(verify_len, r, rm.gamma, nullptr);
-    const int base = request_base(rm, r, L, nullptr);
-    if (base < 0) {
-      accept_len[r] = 0;
-      next_token[r] = -1;
-      continue;
-    }
-    const int32_t *x = draft_tokens + (size_t)r * rm.gamma;
-    int a = 0;
-    while (a < L && stats[base + a].argmax == x[a]) ++a;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rm.B) return;
+  const int L = clamp_len(verify_len, r, rm.gamma, nullptr);
+  const int base = request_base(rm, r, L, nullptr);
+  if (base < 0) {
+    if (lane == 0) { accept_len[r] = 0; next_token[r] = -1; }
+    return;
+  }
+  const int am = lane <= L ? stats[base + lane].argmax : -1;
+  const bool miss = lane < L && am != draft_tokens[(size_t)r * rm.gamma + lane];
+  const unsigned long long mask = __ballot(miss);
+  const int a = mask ? (__ffsll((long long)mask) - 1) : L;
+  // Rows 0..L need L + 1 <= 65 lanes: with gamma = 64 the bonus row is read separately.
+  const int tok = a < kWave ? __shfl(am, a) : stats[base + a].argmax;
+  if (lane == 0) {
     accept_len[r] = a;
-    next_token[r] = stats[base + a].argmax;
-    sumL += L;
-    sumA += a;
-  }
-  red[0][tid] = sumL;
-  red[1][tid] = sumA;
-  __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (tid < off) {
-      red[0][tid] += red[0][tid + off];
-      red[1][tid] += red[1][tid + off];
+    next_token[r] = tok;
+    if (counters) {
+      atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
+      atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)a);
     }
-    __syncthreads();
-  }
-  if (tid == 0 && counters) {
-    atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)red[0][0]);
-    atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)red[1][0]);
   }
 }
 
@@ -460,23 +367,11 @@ hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
   return hipGetLastError();
 }
 
-hipError_t launch_row_merge(const TilePartial *partials, int n_vtiles, int n_vtiles_cap,
-                            const uint16_t *hidden, const uint16_t *W,
-                            const int32_t *draft_tokens, const int32_t *verify_len,
-                            const RowMap &rm, int d, int V, float temperature,
-                            sd_row_stats *stats, WsHeader *ws, hipStream_t stream) {
-  const int cap = rm.B * (rm.gamma + 1);
-  hipLaunchKernelGGL(k_row_merge, dim3((cap + 3) / 4), dim3(256), 0, stream, partials, n_vtiles,
-                     n_vtiles_cap, hidden, W, draft_tokens, verify_len, rm, d, V, temperature,
-                     stats, ws);
-  return hipGetLastError();
-}
-
 hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
                                 const int32_t *verify_len, const RowMap &rm,
                                 int32_t *accept_len, int32_t *next_token, int64_t *counters,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(k_accept_greedy, dim3(1), dim3(256), 0, stream, stats, draft_tokens,
+  hipLaunchKernelGGL(k_accept_greedy, dim3((rm.B + 3) / 4), dim3(256), 0, stream, stats, draft_tokens,
                      verify_len, rm, accept_len, next_token, counters);
   return hipGetLastError();
 }

@@ -28,9 +28,7 @@ int32_t check_sizes(int32_t B, int32_t gamma, int32_t d, int32_t V) {
 }
 
 size_t verify_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
-  const size_t cap = (size_t)B * (gamma + 1);
-  const size_t nvt = (size_t)(V + kMinVocabTile - 1) / kMinVocabTile;
-  return sizeof(WsHeader) + align_up(cap * nvt * sizeof(TilePartial), 256);
+  return verify_workspace_layout(B, gamma, V, nullptr, nullptr);
 }
 
 size_t accept_ws_bytes(int32_t B, int32_t gamma) {
@@ -126,19 +124,27 @@ int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
   if (!workspace || workspace_bytes < verify_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
 
-  hipStream_t s = (hipStream_t)stream;
-  WsHeader *ws = reinterpret_cast<WsHeader *>(workspace);
-  TilePartial *partials = reinterpret_cast<TilePartial *>(reinterpret_cast<char *>(workspace) +
-                                                          sizeof(WsHeader));
-  const int n_vtiles_cap = (V + kMinVocabTile - 1) / kMinVocabTile;
-  RowMap rm{row_offsets, B, gamma};
-  int n_vtiles = 0;
-  hipError_t e = launch_verify_gemm(hidden, lm_head, rm, d, V, temperature, logits, partials,
-                                    n_vtiles_cap, ws, &n_vtiles, s);
-  if (e != hipSuccess) return SD_EDEVICE;
-  e = launch_row_merge(partials, n_vtiles, n_vtiles_cap, hidden, lm_head, draft_tokens,
-                       verify_len, rm, d, V, temperature, stats, ws, s);
-  return launch_status(e);
+  size_t part_off = 0;
+  int part_stride = 0;
+  verify_workspace_layout(B, gamma, V, &part_off, &part_stride);
+  char *wsb = reinterpret_cast<char *>(workspace);
+  VerifyArgs a;
+  a.hidden = hidden;
+  a.W = lm_head;
+  a.draft_tokens = draft_tokens;
+  a.verify_len = verify_len;
+  a.rm = RowMap{row_offsets, B, gamma};
+  a.d = d;
+  a.V = V;
+  a.temperature = temperature;
+  a.scale_log2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
+  a.invT = temperature > 0.f ? 1.0 / (double)temperature : 0.0;
+  a.logits = logits;
+  a.partials = reinterpret_cast<TilePartial *>(wsb + part_off);
+  a.part_stride = part_stride;
+  a.stats = stats;
+  a.ws = reinterpret_cast<WsHeader *>(workspace);
+  return launch_status(launch_verify(a, (hipStream_t)stream));
 }
 
 int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,

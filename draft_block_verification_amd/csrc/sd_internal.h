@@ -79,23 +79,45 @@ __device__ inline void raise_flag(WsHeader *ws, uint32_t bit) {
   if (ws) atomicOr(&ws->flags, bit);
 }
 
+// Kept drafts of request r, clamped to [0, gamma] (flagged when out of range).
+__device__ inline int clamp_len(const int32_t *verify_len, int r, int gamma, WsHeader *ws) {
+  if (!verify_len) return gamma;
+  int L = verify_len[r];
+  if (L < 0 || L > gamma) {
+    raise_flag(ws, SD_FLAG_VERIFY_LEN);
+    L = L < 0 ? 0 : gamma;
+  }
+  return L;
+}
+
 // Order used for argmax: larger value first, then lower index.
 __device__ inline bool beats(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
-hipError_t launch_verify_gemm(const uint16_t *hidden, const uint16_t *W, const RowMap &rm, int d,
-                              int V, float temperature, float *logits, TilePartial *partials,
-                              int n_vtiles_cap, WsHeader *ws, int *n_vtiles_used,
-                              hipStream_t stream);
-int verify_gemm_vocab_tile(int max_rows);
+// Arguments of the LM-head verify kernels (sd_verify_logits).
+struct VerifyArgs {
+  const uint16_t *hidden;       // bf16 [B][gamma + 1][d]
+  const uint16_t *W;            // bf16 [V][d]
+  const int32_t *draft_tokens;  // [B][gamma] or null
+  const int32_t *verify_len;    // [B] or null
+  RowMap rm;
+  int d, V;
+  float temperature;            // 0: greedy statistics only
+  float scale_log2;             // log2(e) / T, or 0
+  double invT;                  // 1 / T, or 0
+  float *logits;                // fp32 [cap][V] or null
+  TilePartial *partials;        // [cap][part_stride]
+  int part_stride;
+  sd_row_stats *stats;          // [cap]
+  WsHeader *ws;
+};
 
-hipError_t launch_row_merge(const TilePartial *partials, int n_vtiles, int n_vtiles_cap,
-                            const uint16_t *hidden, const uint16_t *W,
-                            const int32_t *draft_tokens, const int32_t *verify_len,
-                            const RowMap &rm, int d, int V, float temperature,
-                            sd_row_stats *stats, WsHeader *ws, hipStream_t stream);
+// Bytes of verify workspace (header, then the row partials) for these sizes.
+size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride);
+
+// Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 
 hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
                            int32_t *verify_len, int32_t *row_offsets, hipStream_t stream);

@@ -41,9 +41,10 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_sizes():
-    # Header + one 16-byte partial per (row capacity, 64-wide vocabulary tile).
+    # Header, then one 16-byte partial per (row, 64-wide vocabulary tile).
+    up = lambda x: (x + 255) // 256 * 256
     b = sd.verify_workspace_bytes(1, 9, 2048, 32768)
-    assert b == 256 + ((10 * 512 * 16 + 255) // 256) * 256
+    assert b == 256 + up(10 * 512 * 16)
     assert sd.verify_workspace_bytes(32, 16, 4096, 151936) >= 32 * 17 * (151936 // 64) * 16
     assert sd.accept_workspace_bytes(128, 16, 129280) == 256 + 128 * 16 * 8
     for bad in [(0, 9, 2048, 100), (1, 0, 2048, 100), (1, 65, 2048, 100), (1, 4, 12, 100),
