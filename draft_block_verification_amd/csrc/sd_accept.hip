@@ -99,155 +99,281 @@ __global__ __launch_bounds__(256) void k_accept_greedy(const sd_row_stats *__res
   }
 }
 
-// ------------------------------------------------------- draft-row normaliser
-// One workgroup per kept draft row (r, j < L_r): lse_q = log sum_v exp(l_v / T)
-// over the bf16 drafter logits, with an online max and an fp64 running sum.
-__global__ __launch_bounds__(256) void k_draft_lse(const uint16_t *__restrict__ draft_logits,
-                                                   const int32_t *__restrict__ verify_len, int B,
-                                                   int gamma, int V, float temperature,
-                                                   double *__restrict__ lse_q, WsHeader *ws) {
-  __shared__ float sm[4];
-  __shared__ double ss[4];
-  const int r = blockIdx.x / gamma, j = blockIdx.x - r * gamma;
-  const int L = clamp_len(verify_len, r, gamma, ws);
-  if (j >= L) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t *row = draft_logits + ((size_t)r * gamma + j) * V;
-  const float sl = (float)(kLog2e / (double)temperature);
-  const double invT = 1.0 / (double)temperature;
+// ----------------------------------------------------------- rejection accept
+// Four wide kernels, each over chunks of kChunk vocabulary ids:
+//   k_draft_partial   (chunk, draft row): max and sum of exp((l - max) / T) of the
+//                     drafter logits, for every kept draft row;
+//   k_accept_decide   (request): merge those into log q-normalisers, then accept
+//                     draft j iff u_accept < min(1, p_j(x_j) / q_j(x_j)) and take the
+//                     first rejection a_r (or L_r);
+//   k_draw_partial    (chunk, request): fp64 sums of the draw weights of row a_r --
+//                     max(0, p - q) after a rejection, p for the bonus row;
+//   k_draw_finalize   (request): find the chunk where the running sum crosses
+//                     u_resample * S and scan it for the token.
+constexpr int kChunk = 4096;            // vocabulary ids per chunk
+constexpr int kPer = kChunk / 256;      // ids per thread per chunk
 
-  float m = -INFINITY;
-  double s = 0.0;
-  auto absorb = [&](const float *x, int n) {
-    float cm = x[0];
-    for (int e = 1; e < n; ++e) cm = fmaxf(cm, x[e]);
-    if (cm > m) {
-      if (s != 0.0) s *= exp(((double)m - (double)cm) * invT);
-      m = cm;
-    }
-    float part = 0.f;
-    for (int e = 0; e < n; ++e) part += exp2f((x[e] - m) * sl);
-    s += (double)part;
-  };
-  if ((V & 7) == 0) {
-    const int nch = V >> 3;
-    for (int c = tid; c < nch; c += 256) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(row + (size_t)c * 8);
-      float x[8];
+struct DraftPart {
+  float m;       // max drafter logit of the chunk (raw, before / T)
+  float pad;
+  double s;      // sum over the chunk of exp((l - m) / T)
+};
+
+struct RejArgs {
+  const float *logits;
+  const sd_row_stats *stats;
+  const uint16_t *draft_logits;
+  const int32_t *draft_tokens;
+  const int32_t *verify_len;
+  RowMap rm;
+  const float *u_accept, *u_resample;
+  int V, C;                  // vocabulary size, chunks per row
+  float sl;                  // log2(e) / T
+  double invT;               // 1 / T
+  int32_t *accept_len, *next_token;
+  int64_t *counters;
+  double *lse_q;             // [B][gamma]
+  int32_t *acc_a;            // [B] accepted length, -1 for a request outside the row capacity
+  DraftPart *dpart;          // [B][gamma][C]
+  double *csum;              // [B][C][2]: residual (or bonus) weight sum, p weight sum
+  WsHeader *ws;
+};
+
+__device__ inline double block_sum_d(double x, double *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const double r = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float block_max_f(float x, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// This thread's kPer drafter logits of chunk c (-inf past V).
+__device__ inline void load_draft_chunk(const uint16_t *row, int V, int c, float *x) {
+  const int v0 = c * kChunk + threadIdx.x * kPer;
+  if ((V & 7) == 0 && v0 + kPer <= V) {
+#pragma unroll
+    for (int h = 0; h < kPer / 8; ++h) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v0 + 8 * h);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        x[2 * q] = __uint_as_float(w[q] << 16);
-        x[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        x[8 * h + 2 * q] = __uint_as_float(w[q] << 16);
+        x[8 * h + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
       }
-      absorb(x, 8);
     }
   } else {
-    for (int v = tid; v < V; v += 256) {
-      const float x = bf16_to_f32(row[v]);
-      absorb(&x, 1);
-    }
-  }
-  // Combine (max, sum) pairs: wave butterfly, then the four waves in order.
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float om = __shfl_xor(m, off);
-    const double os = __shfl_xor(s, off);
-    const float nm = fmaxf(m, om);
-    double ns = 0.0;
-    if (s != 0.0) ns += s * exp(((double)m - (double)nm) * invT);
-    if (os != 0.0) ns += os * exp(((double)om - (double)nm) * invT);
-    m = nm;
-    s = ns;
-  }
-  if (lane == 0) { sm[wave] = m; ss[wave] = s; }
-  __syncthreads();
-  if (tid == 0) {
-    float M = sm[0];
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w]);
-    double S = 0.0;
-    for (int w = 0; w < 4; ++w)
-      if (ss[w] != 0.0) S += ss[w] * exp(((double)sm[w] - (double)M) * invT);
-    lse_q[(size_t)r * gamma + j] = (double)M * invT + log(S);
+    for (int e = 0; e < kPer; ++e) x[e] = v0 + e < V ? bf16_to_f32(row[v0 + e]) : -INFINITY;
   }
 }
 
-// ----------------------------------------------------------- rejection accept
-constexpr int kTileElems = 256 * 8;   // elements per scan tile (8 per thread)
-constexpr int kMaxTiles = 1024;       // V <= 2^21 in the sampler
+__global__ __launch_bounds__(256) void k_draft_partial(RejArgs a) {
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  const int gamma = a.rm.gamma;
+  const int r = blockIdx.y / gamma, j = blockIdx.y - r * gamma, c = blockIdx.x;
+  const int L = clamp_len(a.verify_len, r, gamma, threadIdx.x == 0 ? a.ws : nullptr);
+  if (j >= L) return;
+  const uint16_t *row = a.draft_logits + ((size_t)r * gamma + j) * a.V;
+  float x[kPer];
+  load_draft_chunk(row, a.V, c, x);
+  float cm = x[0];
+#pragma unroll
+  for (int e = 1; e < kPer; ++e) cm = fmaxf(cm, x[e]);
+  const float M = block_max_f(cm, redf);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (x[e] != -INFINITY) s += exp2f((x[e] - M) * a.sl);
+  const double S = block_sum_d((double)s, redd);
+  if (threadIdx.x == 0) {
+    DraftPart p;
+    p.m = M; p.pad = 0.f; p.s = S;
+    a.dpart[((size_t)r * gamma + j) * a.C + c] = p;
+  }
+}
 
-struct SampleRow {
-  const float *z;         // target logits of the sampled row [V]
-  const uint16_t *q;      // drafter logits of the row [V], or null for a plain p draw
+__global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
+  __shared__ int s_rej[64];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gamma = a.rm.gamma;
+  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  const int base = request_base(a.rm, r, L, tid == 0 ? a.ws : nullptr);
+  if (base < 0) {
+    if (tid == 0) { a.acc_a[r] = -1; a.accept_len[r] = 0; a.next_token[r] = -1; }
+    return;
+  }
+  for (int j = wave; j < L; j += 4) {
+    const DraftPart *P = a.dpart + ((size_t)r * gamma + j) * a.C;
+    float M = -INFINITY;
+    for (int c = lane; c < a.C; c += kWave) M = fmaxf(M, P[c].m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    double S = 0.0;
+    for (int c = lane; c < a.C; c += kWave) {
+      const DraftPart q = P[c];
+      if (q.s != 0.0) S += q.s * exp(((double)q.m - (double)M) * a.invT);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    if (lane == 0) {
+      const double lse = (double)M * a.invT + log(S);
+      a.lse_q[(size_t)r * gamma + j] = lse;
+      const int x = a.draft_tokens[(size_t)r * gamma + j];
+      int rej = 1;
+      if (x >= 0 && x < a.V) {
+        const sd_row_stats st = a.stats[base + j];
+        const double lx = (double)bf16_to_f32(a.draft_logits[((size_t)r * gamma + j) * a.V + x]);
+        const double logp = st.z_draft * a.invT - st.lse;
+        const double logq = lx * a.invT - lse;
+        const double ratio = exp(logp - logq);
+        rej = !((double)a.u_accept[(size_t)r * gamma + j] < fmin(1.0, ratio));
+      }
+      s_rej[j] = rej;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = L;
+    for (int j = 0; j < L; ++j)
+      if (s_rej[j]) { acc = j; break; }
+    a.acc_a[r] = acc;
+    a.accept_len[r] = acc;
+    if (a.counters) {
+      atomicAdd(reinterpret_cast<unsigned long long *>(a.counters), (unsigned long long)L);
+      atomicAdd(reinterpret_cast<unsigned long long *>(a.counters + 1), (unsigned long long)acc);
+    }
+  }
+}
+
+// The row being drawn from for request r: a_r after a rejection (residual), L_r otherwise.
+struct DrawRow {
+  const float *z;        // target logits of the row
+  const uint16_t *q;     // drafter logits of the row (residual draws), else null
   double lse_p, lse_q, invT;
 };
 
-// Weight of vocabulary id v: p_v for a plain draw, max(0, p_v - q_v) for a residual.
-__device__ inline float draw_weight(const SampleRow &sr, int v) {
-  const float p = expf((float)((double)sr.z[v] * sr.invT - sr.lse_p));
-  if (!sr.q) return p;
-  const float q = expf((float)((double)bf16_to_f32(sr.q[v]) * sr.invT - sr.lse_q));
-  return fmaxf(p - q, 0.f);
+__device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow) {
+  const int acc = a.acc_a[r];
+  if (acc < 0) return false;
+  const int gamma = a.rm.gamma;
+  const int L = clamp_len(a.verify_len, r, gamma, nullptr);
+  const int base = request_base(a.rm, r, L, nullptr);
+  d->z = a.logits + (size_t)(base + acc) * a.V;
+  d->lse_p = a.stats[base + acc].lse;
+  d->invT = a.invT;
+  d->q = nullptr;
+  d->lse_q = 0.0;
+  if (acc < L) {
+    d->q = a.draft_logits + ((size_t)r * gamma + acc) * a.V;
+    d->lse_q = a.lse_q[(size_t)r * gamma + acc];
+  }
+  *arow = base + acc;
+  return true;
 }
 
-// Inverse-CDF draw in ascending vocabulary id: the smallest v whose running weight
-// exceeds u * S (S = total weight). All 256 threads call it and get the same id;
-// -1 when the total weight is zero. If rounding leaves no such v, the last id with
-// positive weight is taken.
-//   Pass 1: per-thread sums of 8 consecutive ids per 2048-id tile, reduced to tile
-//           totals in a fixed order; thread 0 finds the tile where the running
-//           total crosses u * S.
-//   Pass 2: an exclusive scan inside that tile locates the id.
-__device__ int inverse_cdf_draw(const SampleRow &sr, int V, float u, double *tile_sum,
-                                double *wave_part, double *scal, int *sel) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntiles = (V + kTileElems - 1) / kTileElems;
-  for (int t = 0; t < ntiles; ++t) {
-    const int v0 = t * kTileElems + tid * 8;
-    double part = 0.0;
-    for (int e = 0; e < 8; ++e)
-      if (v0 + e < V) part += (double)draw_weight(sr, v0 + e);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    if (lane == 0) wave_part[t * 4 + wave] = part;
+// p_v, and max(0, p_v - q_v) when the row has drafter logits.
+__device__ inline void draw_weights(const DrawRow &d, int v, float *p, float *res) {
+  *p = expf((float)((double)d.z[v] * d.invT - d.lse_p));
+  *res = *p;
+  if (d.q) {
+    const float q = expf((float)((double)bf16_to_f32(d.q[v]) * d.invT - d.lse_q));
+    *res = fmaxf(*p - q, 0.f);
   }
-  __syncthreads();
-  if (tid == 0) {
-    double S = 0.0;
-    for (int t = 0; t < ntiles; ++t) {
-      tile_sum[t] = ((wave_part[4 * t] + wave_part[4 * t + 1]) + wave_part[4 * t + 2]) +
-                    wave_part[4 * t + 3];
-      S += tile_sum[t];
+}
+
+__global__ __launch_bounds__(256) void k_draw_partial(RejArgs a) {
+  __shared__ double red[4];
+  const int r = blockIdx.y, c = blockIdx.x;
+  DrawRow d;
+  int arow;
+  if (!draw_row(a, r, &d, &arow)) return;
+  const int v0 = c * kChunk + threadIdx.x * kPer;
+  double sr = 0.0, sp = 0.0;
+  for (int e = 0; e < kPer; ++e) {
+    if (v0 + e < a.V) {
+      float p, w;
+      draw_weights(d, v0 + e, &p, &w);
+      sr += (double)w;
+      sp += (double)p;
     }
-    const double thresh = (double)u * S;
+  }
+  sr = block_sum_d(sr, red);
+  sp = block_sum_d(sp, red);
+  if (threadIdx.x == 0) {
+    a.csum[((size_t)r * a.C + c) * 2] = sr;
+    a.csum[((size_t)r * a.C + c) * 2 + 1] = sp;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
+  __shared__ double s_d[8];
+  __shared__ int s_i[12];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  DrawRow d;
+  int arow;
+  if (!draw_row(a, r, &d, &arow)) return;
+  const int gamma = a.rm.gamma;
+  const int acc = a.acc_a[r];
+  const double *cs = a.csum + (size_t)r * a.C * 2;
+  if (tid == 0) {
+    int col = 0;
+    double S = 0.0;
+    for (int c = 0; c < a.C; ++c) S += cs[2 * c];
+    if (S == 0.0 && d.q) {            // no residual mass (p == q at this row): draw from p
+      raise_flag(a.ws, SD_FLAG_NO_RESIDUAL);
+      col = 1;
+      S = 0.0;
+      for (int c = 0; c < a.C; ++c) S += cs[2 * c + 1];
+    }
+    const double thresh = (double)a.u_resample[(size_t)r * (gamma + 1) + acc] * S;
     int hit = -1, last_pos = 0;
     double carry = 0.0;
     if (S > 0.0) {
-      for (int t = 0; t < ntiles; ++t) {
-        if (carry + tile_sum[t] > thresh) { hit = t; break; }
-        carry += tile_sum[t];
+      for (int c = 0; c < a.C; ++c) {
+        if (carry + cs[2 * c + col] > thresh) { hit = c; break; }
+        carry += cs[2 * c + col];
       }
-      if (hit < 0) {
+      if (hit < 0) {                  // rounding: the last id with positive weight
         last_pos = 1;
-        for (int t = ntiles - 1; t >= 0; --t)
-          if (tile_sum[t] > 0.0) { hit = t; break; }
+        for (int c = a.C - 1; c >= 0; --c)
+          if (cs[2 * c + col] > 0.0) { hit = c; break; }
       }
     }
-    sel[0] = hit;
-    sel[1] = last_pos;
-    scal[0] = carry;
-    scal[1] = thresh;
+    s_i[0] = hit; s_i[1] = last_pos; s_i[2] = col;
+    s_d[0] = carry; s_d[1] = thresh;
   }
   __syncthreads();
-  const int hit = sel[0], last_pos = sel[1];
-  if (hit < 0) return -1;
-  const double carry = scal[0], thresh = scal[1];
-
-  const int v0 = hit * kTileElems + tid * 8;
-  float w[8];
+  const int hit = s_i[0], last_pos = s_i[1], col = s_i[2];
+  if (hit < 0) {                      // no weight at all: fall back to the target argmax
+    if (tid == 0) a.next_token[r] = a.stats[arow].argmax;
+    return;
+  }
+  if (col == 1) d.q = nullptr;
+  const double carry = s_d[0], thresh = s_d[1];
+  // Scan the crossing chunk: kPer consecutive ids per thread, exclusive scan of the
+  // per-thread sums, then the crossing thread walks its ids.
+  const int v0 = hit * kChunk + tid * kPer;
+  float w[kPer];
   double mine = 0.0;
-  for (int e = 0; e < 8; ++e) {
-    w[e] = (v0 + e < V) ? draw_weight(sr, v0 + e) : 0.f;
-    mine += (double)w[e];
+  for (int e = 0; e < kPer; ++e) {
+    float p = 0.f, x = 0.f;
+    if (v0 + e < a.V) draw_weights(d, v0 + e, &p, &x);
+    w[e] = x;
+    mine += (double)x;
   }
   double incl = mine;
 #pragma unroll
@@ -255,18 +381,17 @@ __device__ int inverse_cdf_draw(const SampleRow &sr, int V, float u, double *til
     const double o = __shfl_up(incl, off);
     if (lane >= off) incl += o;
   }
-  if (lane == 63) scal[2 + wave] = incl;
+  if (lane == 63) s_d[2 + wave] = incl;
   __syncthreads();
   double before = 0.0;
-  for (int q = 0; q < wave; ++q) before += scal[2 + q];
+  for (int q = 0; q < wave; ++q) before += s_d[2 + q];
   const double base = carry + (before + (incl - mine));
-
   int cross = 0x7fffffff, lastp = -1;
-  for (int e = 7; e >= 0; --e)
+  for (int e = kPer - 1; e >= 0; --e)
     if (w[e] > 0.f) { lastp = v0 + e; break; }
   if (!last_pos && base + mine > thresh) {
     double run = 0.0;
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kPer; ++e) {
       run += (double)w[e];
       if (base + run > thresh) { cross = v0 + e; break; }
     }
@@ -277,84 +402,12 @@ __device__ int inverse_cdf_draw(const SampleRow &sr, int V, float u, double *til
     cross = min(cross, __shfl_xor(cross, off));
     lastp = max(lastp, __shfl_xor(lastp, off));
   }
-  if (lane == 0) { sel[2 + wave] = cross; sel[6 + wave] = lastp; }
+  if (lane == 0) { s_i[4 + wave] = cross; s_i[8 + wave] = lastp; }
   __syncthreads();
-  int c = sel[2], l = sel[6];
-  for (int q = 1; q < 4; ++q) { c = min(c, sel[2 + q]); l = max(l, sel[6 + q]); }
-  __syncthreads();   // sel / scal are reused by the next call
-  return (!last_pos && c != 0x7fffffff) ? c : l;
-}
-
-__global__ __launch_bounds__(256) void k_accept_rejection(
-    const float *__restrict__ logits, const sd_row_stats *__restrict__ stats,
-    const uint16_t *__restrict__ draft_logits, const int32_t *__restrict__ draft_tokens,
-    const int32_t *__restrict__ verify_len, RowMap rm, const float *__restrict__ u_accept,
-    const float *__restrict__ u_resample, int V, float temperature,
-    const double *__restrict__ lse_q, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ next_token, int64_t *__restrict__ counters, WsHeader *ws) {
-  __shared__ double tile_sum[kMaxTiles];
-  __shared__ double wave_part[4 * kMaxTiles];
-  __shared__ double scal[8];
-  __shared__ int sel[12];
-  __shared__ int s_a;
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int gamma = rm.gamma;
-  const int L = clamp_len(verify_len, r, gamma, tid == 0 ? ws : nullptr);
-  const int base = request_base(rm, r, L, tid == 0 ? ws : nullptr);
-  if (base < 0) {
-    if (tid == 0) { accept_len[r] = 0; next_token[r] = -1; }
-    return;
-  }
-  const double invT = 1.0 / (double)temperature;
-
-  if (tid < kWave) {
-    bool rejected = false;
-    if (lane < L) {
-      const sd_row_stats st = stats[base + lane];
-      const int x = draft_tokens[(size_t)r * gamma + lane];
-      if (x < 0 || x >= V) {
-        rejected = true;
-      } else {
-        const size_t qrow = ((size_t)r * gamma + lane) * V;
-        const double lx = (double)bf16_to_f32(draft_logits[qrow + x]);
-        const double logp = st.z_draft * invT - st.lse;
-        const double logq = lx * invT - lse_q[(size_t)r * gamma + lane];
-        const double ratio = exp(logp - logq);
-        rejected = !((double)u_accept[(size_t)r * gamma + lane] < fmin(1.0, ratio));
-      }
-    }
-    const unsigned long long mask = __ballot(rejected);
-    if (lane == 0) s_a = mask ? (__ffsll(mask) - 1) : L;
-  }
-  __syncthreads();
-  const int a = s_a;
-
-  SampleRow sr;
-  sr.z = logits + (size_t)(base + a) * V;
-  sr.lse_p = stats[base + a].lse;
-  sr.invT = invT;
-  sr.q = nullptr;
-  sr.lse_q = 0.0;
-  const float u = u_resample[(size_t)r * (gamma + 1) + a];
-  int tok = -1;
-  if (a < L) {
-    sr.q = draft_logits + ((size_t)r * gamma + a) * V;
-    sr.lse_q = lse_q[(size_t)r * gamma + a];
-    tok = inverse_cdf_draw(sr, V, u, tile_sum, wave_part, scal, sel);
-    if (tok < 0) {
-      if (tid == 0) raise_flag(ws, SD_FLAG_NO_RESIDUAL);
-      sr.q = nullptr;
-    }
-  }
-  if (tok < 0) tok = inverse_cdf_draw(sr, V, u, tile_sum, wave_part, scal, sel);
-  if (tok < 0) tok = stats[base + a].argmax;
   if (tid == 0) {
-    accept_len[r] = a;
-    next_token[r] = tok;
-    if (counters) {
-      atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
-      atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)a);
-    }
+    int c = s_i[4], l = s_i[8];
+    for (int q = 1; q < 4; ++q) { c = min(c, s_i[4 + q]); l = max(l, s_i[8 + q]); }
+    a.next_token[r] = (!last_pos && c != 0x7fffffff) ? c : l;
   }
 }
 
@@ -376,20 +429,57 @@ hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_
   return hipGetLastError();
 }
 
+size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay) {
+  const int C = (V + kChunk - 1) / kChunk;
+  AcceptLayout l;
+  l.chunks = C;
+  l.lse_q = sizeof(WsHeader);
+  l.acc_a = align_up(l.lse_q + (size_t)B * gamma * sizeof(double), 256);
+  l.dpart = align_up(l.acc_a + (size_t)B * sizeof(int32_t), 256);
+  l.csum = align_up(l.dpart + (size_t)B * gamma * C * sizeof(DraftPart), 256);
+  const size_t total = align_up(l.csum + (size_t)B * C * 2 * sizeof(double), 256);
+  if (lay) *lay = l;
+  return total;
+}
+
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
                                    const uint16_t *draft_logits, const int32_t *draft_tokens,
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
-                                   int64_t *counters, double *lse_q, WsHeader *ws,
-                                   hipStream_t stream) {
-  hipLaunchKernelGGL(k_draft_lse, dim3(rm.B * rm.gamma), dim3(256), 0, stream, draft_logits,
-                     verify_len, rm.B, rm.gamma, V, temperature, lse_q, ws);
+                                   int64_t *counters, void *workspace, hipStream_t stream) {
+  AcceptLayout l;
+  accept_workspace_layout(rm.B, rm.gamma, V, &l);
+  char *w = reinterpret_cast<char *>(workspace);
+  RejArgs a;
+  a.logits = logits;
+  a.stats = stats;
+  a.draft_logits = draft_logits;
+  a.draft_tokens = draft_tokens;
+  a.verify_len = verify_len;
+  a.rm = rm;
+  a.u_accept = u_accept;
+  a.u_resample = u_resample;
+  a.V = V;
+  a.C = l.chunks;
+  a.sl = (float)(kLog2e / (double)temperature);
+  a.invT = 1.0 / (double)temperature;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.counters = counters;
+  a.lse_q = reinterpret_cast<double *>(w + l.lse_q);
+  a.acc_a = reinterpret_cast<int32_t *>(w + l.acc_a);
+  a.dpart = reinterpret_cast<DraftPart *>(w + l.dpart);
+  a.csum = reinterpret_cast<double *>(w + l.csum);
+  a.ws = reinterpret_cast<WsHeader *>(workspace);
+  hipLaunchKernelGGL(k_draft_partial, dim3(l.chunks, rm.B * rm.gamma), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_accept_rejection, dim3(rm.B), dim3(256), 0, stream, logits, stats,
-                     draft_logits, draft_tokens, verify_len, rm, u_accept, u_resample, V,
-                     temperature, lse_q, accept_len, next_token, counters, ws);
+  hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_draw_partial, dim3(l.chunks, rm.B), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_draw_finalize, dim3(rm.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

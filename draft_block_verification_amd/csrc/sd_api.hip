@@ -31,8 +31,8 @@ size_t verify_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
   return verify_workspace_layout(B, gamma, V, nullptr, nullptr);
 }
 
-size_t accept_ws_bytes(int32_t B, int32_t gamma) {
-  return sizeof(WsHeader) + align_up((size_t)B * gamma * sizeof(double), 256);
+size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
+  return accept_workspace_layout(B, gamma, V, nullptr);
 }
 
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? SD_OK : SD_EDEVICE; }
@@ -74,7 +74,7 @@ size_t sd_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t d, int32_t V)
 
 size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
   if (check_sizes(B, gamma, 8, V) != SD_OK) return 0;
-  return accept_ws_bytes(B, gamma);
+  return accept_ws_bytes(B, gamma, V);
 }
 
 int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
@@ -181,16 +181,13 @@ int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
       !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
       (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
     return SD_EALIGN;
-  if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma)) return SD_EWORKSPACE;
+  if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
-  WsHeader *ws = reinterpret_cast<WsHeader *>(workspace);
-  double *lse_q = reinterpret_cast<double *>(reinterpret_cast<char *>(workspace) +
-                                             sizeof(WsHeader));
   RowMap rm{row_offsets, B, gamma};
   return launch_status(launch_accept_rejection(logits, stats, draft_logits, draft_tokens,
                                                verify_len, rm, u_accept, u_resample, V,
                                                temperature, accept_len, next_token, counters,
-                                               lse_q, ws, (hipStream_t)stream));
+                                               workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -287,76 +287,83 @@ __global__ __launch_bounds__(256) void k_gemm_stream(VerifyArgs a) {
 }
 
 // ----------------------------------------------------------------- tiled regime
+// BM x BN output tiles; four waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2)
+// block of 16x16x32 MFMA tiles with its accumulators in registers. K advances in
+// steps of 64 through double-buffered LDS: the global loads of step kt+1 are issued
+// before step kt is computed and written to LDS after it. LDS rows are 128 bytes and
+// a row's 16-byte chunk index is XORed with (row >> 1) & 7, so fragment reads of 16
+// consecutive rows hit 16 different bank groups. Blocks are renumbered so the M-tiles
+// of one vocabulary tile run back to back on the same XCD and share its L2.
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a) {
-  constexpr int BK = 64, LDK = BK + 8;
-  constexpr int WM = 2, WN = 2;
-  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  constexpr int A_CH = BM * (BK / 8) / 256, B_CH = BN * (BK / 8) / 256;
-  constexpr int LDC = BN + 4;
-  constexpr int STAGE_BYTES = 2 * (BM + BN) * LDK * 2;
-  constexpr int C_BYTES = BM * LDC * 4;
-  constexpr int SMEM = STAGE_BYTES > C_BYTES ? STAGE_BYTES : C_BYTES;
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for 256 threads");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  uint16_t *As = reinterpret_cast<uint16_t *>(smem);          // [2][BM][LDK]
-  uint16_t *Bs = As + 2 * BM * LDK;                            // [2][BN][LDK]
-  float *Cs = reinterpret_cast<float *>(smem);                 // [BM][LDC] after the K loop
+__global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a, int n_mt, int n_nt) {
+  constexpr int BK = 64, CH = BK / 8;
+  constexpr int TM = BM / 32, TN = BN / 32;
+  constexpr int A_LD = BM * CH / 256, B_LD = BN * CH / 256;
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
+  static_assert(BM * 32 <= 2 * STAGE * 2, "epilogue exchange fits in the stage buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t S[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int v0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Hardware hands consecutive block ids to the 8 XCDs in turn; give each XCD a
+  // contiguous range of logical tiles (M fastest).
+  const int nb = n_mt * n_nt, hb = blockIdx.x;
+  const int per = nb / 8, rem = nb % 8, xcd = hb % 8, pos = hb / 8;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + pos;
+  const int mt = logical % n_mt, nt = logical / n_mt;
+  const int m0 = mt * BM, v0 = nt * BN;
   const int M = rows_total(a.rm);
   const int d = a.d, V = a.V;
   if (m0 >= M) return;
 
-  const uint16_t *asrc[A_CH];
-  int a_lds[A_CH], a_k[A_CH];
+  // Per-thread load sources (row start + chunk) and swizzled LDS offsets.
+  const uint16_t *a_src[A_LD], *b_src[B_LD];
+  int a_off[A_LD], b_off[B_LD], a_c[A_LD], b_c[B_LD];
 #pragma unroll
-  for (int c = 0; c < A_CH; ++c) {
-    const int ch = tid + 256 * c, rr = ch >> 3, kc = (ch & 7) * 8;
-    a_lds[c] = rr * LDK + kc;
-    a_k[c] = kc;
-    asrc[c] = nullptr;
-    const int m = m0 + rr;
+  for (int i = 0; i < A_LD; ++i) {
+    const int e = tid + 256 * i, r = e / CH, c = e % CH;
+    const int m = m0 + r;
+    int hr = -1;
     if (m < M) {
-      int r, j;
-      const int hr = hidden_row(a.rm, m, &r, &j);
-      if (hr >= 0) asrc[c] = a.hidden + (size_t)hr * d;
-      else raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      int rq, j;
+      hr = hidden_row(a.rm, m, &rq, &j);
+      if (hr < 0) raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
     }
+    a_src[i] = a.hidden + (size_t)(hr >= 0 ? hr : 0) * d;   // rows past M: any valid row
+    a_c[i] = 8 * c;
+    a_off[i] = r * BK + 8 * (c ^ ((r >> 1) & 7));
   }
-  const uint16_t *bsrc[B_CH];
-  int b_lds[B_CH], b_k[B_CH];
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) {
-    const int ch = tid + 256 * c, rr = ch >> 3, kc = (ch & 7) * 8;
-    b_lds[c] = rr * LDK + kc;
-    b_k[c] = kc;
-    bsrc[c] = a.W + (size_t)min(v0 + rr, V - 1) * d;
+  for (int i = 0; i < B_LD; ++i) {
+    const int e = tid + 256 * i, r = e / CH, c = e % CH;
+    b_src[i] = a.W + (size_t)min(v0 + r, V - 1) * d;
+    b_c[i] = 8 * c;
+    b_off[i] = BM * BK + r * BK + 8 * (c ^ ((r >> 1) & 7));
   }
 
-  u32x4 ra[A_CH], rb[B_CH];
+  u32x4 ra[A_LD], rb[B_LD];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int k = k0 + a_k[c];
-      ra[c] = (asrc[c] && k < d) ? *reinterpret_cast<const u32x4 *>(asrc[c] + k) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < A_LD; ++i) {
+      const int k = k0 + a_c[i];
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(a_src[i] + min(k, d - 8));
+      ra[i] = k < d ? v : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int k = k0 + b_k[c];
-      rb[c] = (k < d) ? *reinterpret_cast<const u32x4 *>(bsrc[c] + k) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < B_LD; ++i) {
+      const int k = k0 + b_c[i];
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(b_src[i] + min(k, d - 8));
+      rb[i] = k < d ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto sstore = [&](int buf) {
+    uint16_t *Sb = S + buf * STAGE;
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c)
-      *reinterpret_cast<u32x4 *>(As + buf * BM * LDK + a_lds[c]) = ra[c];
+    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4 *>(Sb + a_off[i]) = ra[i];
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c)
-      *reinterpret_cast<u32x4 *>(Bs + buf * BN * LDK + b_lds[c]) = rb[c];
+    for (int i = 0; i < B_LD; ++i) *reinterpret_cast<u32x4 *>(Sb + b_off[i]) = rb[i];
   };
 
   f32x4 acc[TM][TN];
@@ -366,53 +373,289 @@ __global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a) {
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (d + BK - 1) / BK;
+  const int fr = lane & 15, fc = lane >> 4;
+  // All fragments of one K step (two 32-wide substeps) are read before any MFMA of
+  // the step, so LDS latency overlaps the first substep's MFMAs.
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto read_frags = [&](int buf) {
+    const uint16_t *Ab = S + buf * STAGE;
+    const uint16_t *Bb = Ab + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 4 * ks + fc;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + i * 16 + fr;
+        af[ks][i] = load8(Ab + r * BK + 8 * (c ^ ((r >> 1) & 7)));
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * (BN / 2) + t * 16 + fr;
+        bfr[ks][t] = load8(Bb + r * BK + 8 * (c ^ ((r >> 1) & 7)));
+      }
+    }
+  };
   gload(0);
   sstore(0);
   __syncthreads();
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t *Ab = As + buf * BM * LDK;
-    const uint16_t *Bb = Bs + buf * BN * LDK;
+    read_frags(buf);
+    gload(min(kt + 1, nk - 1));      // past the end: a harmless reload, stored to an unused buffer
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[TM], bfr[TN];
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = load8(Ab + (wm * TM * 16 + i * 16 + frag_row) * LDK + ks * 32 + frag_k);
 #pragma unroll
-      for (int t = 0; t < TN; ++t)
-        bfr[t] = load8(Bb + (wn * TN * 16 + t * 16 + frag_row) * LDK + ks * 32 + frag_k);
+        for (int t = 0; t < TN; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][t], acc[i][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue from registers. Lane l holds rows wm*BM/2 + i*16 + 4*(l>>4) + q and
+  // columns wn*BN/2 + t*16 + (l & 15).
+  const int colb = v0 + wn * (BN / 2) + fr;
+  if (a.logits) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * (BM / 2) + i * 16 + 4 * fc + q;
+        if (m < M) {
+          float *dst = a.logits + (size_t)m * V;
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            if (colb + t * 16 < V) dst[colb + t * 16] = acc[i][t][q];
+        }
+      }
+  }
+  // Row statistics over this wave's BN/2 columns, then across the two waves of a row.
+  float *X = reinterpret_cast<float *>(S);   // [2][BM][4]: t1, t2, arg (bits), sum
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t1 = -INFINITY, t2 = -INFINITY;
+      int a1 = 0x7fffffff;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int v = colb + t * 16;
+        const float z = acc[i][t][q];
+        if (v < V) {
+          if (beats(z, v, t1, a1)) { t2 = t1; t1 = z; a1 = v; }
+          else if (z > t2) t2 = z;
+        }
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+        const int oa = __shfl_xor(a1, off);
+        if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+        else { t2 = fmaxf(t2, o1); }
+      }
+      float s = 0.f;
+      if (a.scale_log2 > 0.f) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          if (colb + t * 16 < V) s += exp2f((acc[i][t][q] - t1) * a.scale_log2);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      }
+      if (fr == 0) {
+        const int rl = wm * (BM / 2) + i * 16 + 4 * fc + q;
+        float *x = X + (wn * BM + rl) * 4;
+        x[0] = t1; x[1] = t2; x[2] = __int_as_float(a1); x[3] = s;
+      }
+    }
+  __syncthreads();
+  for (int rl = tid; rl < BM; rl += 256) {
+    const int m = m0 + rl;
+    if (m >= M) continue;
+    const float *x0 = X + rl * 4, *x1 = X + (BM + rl) * 4;
+    RowAcc r0{x0[0], x0[1], x0[3], __float_as_int(x0[2])};
+    const RowAcc r1{x1[0], x1[1], x1[3], __float_as_int(x1[2])};
+    row_acc_merge(r0, r1, a.scale_log2);
+    TilePartial p;
+    p.top1 = r0.t1; p.top2 = r0.t2; p.arg = r0.arg; p.sum = r0.sum;
+    a.partials[(size_t)m * a.part_stride + nt] = p;
+  }
+}
+
+// ------------------------------------------------------ direct-to-LDS regime
+// The tiled GEMM for d % BK == 0 and many rows. global_load_lds_dwordx4 moves each
+// wave load's 1 KB straight into one of NS LDS stage buffers (no registers held), so
+// NS-1 K steps are in flight per block. Each K step: wait for this thread's loads of
+// the step (explicit vmcnt), one workgroup barrier, refill the buffer consumed in the
+// previous step, then read fragments and run the MFMAs. NW = 8 waves (2 x 4) give
+// two waves per SIMD, which hides LDS read latency behind the other wave's MFMAs.
+// Rows of a stage are BK/8 16-byte chunks; chunk j of row r holds logical chunk
+// j ^ swz(r), so the MFMA fragment reads of 16 rows spread over the bank groups.
+#define LDSP __attribute__((address_space(3)))
+#define GLBP __attribute__((address_space(1)))
+template <int BM, int BN, int BK, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, int n_nt) {
+  constexpr int NT = 64 * NW;                      // threads
+  constexpr int WNG = NW / 2;                      // waves along N (2 along M)
+  constexpr int CH = BK / 8;                       // 16-byte chunks per row per stage
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * BK;                 // bf16 per stage
+  constexpr int DPT = ROWS * CH / NT;              // DMA instructions per thread per stage
+  constexpr int RPI = 64 / CH;                     // rows per wave instruction
+  constexpr int TM = BM / 32, TN = BN / WNG / 16;
+  // 16 consecutive rows read at one chunk index land in 16 different bank groups.
+  auto swz = [](int r) { return (r >> (CH == 4 ? 2 : 1)) & (CH - 1); };
+  static_assert(ROWS * CH % NT == 0, "stage splits over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t S[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WNG, wn = wave % WNG;
+  const int nb = n_mt * n_nt, hb = blockIdx.x;
+  const int per = nb / 8, rem = nb % 8, xcd = hb % 8, pos = hb / 8;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + pos;
+  const int mt = logical % n_mt, nt = logical / n_mt;
+  const int m0 = mt * BM, v0 = nt * BN;
+  const int M = rows_total(a.rm);
+  const int d = a.d, V = a.V;
+  if (m0 >= M) return;
+
+  // DMA i of this thread: wave instruction w + 4 i covers rows RPI*(w + 4 i) .. + RPI - 1;
+  // lane l fills LDS slot l: row r = base + l / CH, stored chunk j = l % CH, which holds
+  // logical chunk j ^ swz(r).
+  const uint16_t *src[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    const int r = RPI * (wave + NW * i) + lane / CH, j = lane % CH;
+    const int c = j ^ swz(r);
+    const uint16_t *row;
+    if (r < BM) {
+      const int m = m0 + r;
+      int hr = -1;
+      if (m < M) { int rq, jj; hr = hidden_row(a.rm, m, &rq, &jj); }
+      row = a.hidden + (size_t)(hr >= 0 ? hr : 0) * d;
+    } else {
+      row = a.W + (size_t)min(v0 + r - BM, V - 1) * d;
+    }
+    src[i] = row + 8 * c;
+  }
+  const int nk = d / BK;                            // d % BK == 0 required
+  auto issue = [&](int kt) {
+    const int kk = min(kt, nk - 1) * BK;            // past the end: reload the last step (unused)
+    LDSP uint16_t *dst = (LDSP uint16_t *)S + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i)
+      __builtin_amdgcn_global_load_lds((const GLBP void *)(src[i] + kk),
+                                       (LDSP void *)(dst + (wave + NW * i) * 512), 16, 0, 0);
+  };
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt is complete once at most (NS-2)*DPT newer DMAs of this thread are pending.
+    constexpr int PEND = (NS - 2) * DPT;
+    __builtin_amdgcn_s_waitcnt((PEND & 15) | (((PEND >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(kt + NS - 1);          // refills the buffer read in the previous iteration
+    const LDSP uint16_t *Ab = (const LDSP uint16_t *)S + (kt % NS) * STAGE;
+    const LDSP uint16_t *Bb = Ab + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int c = 4 * ks + fc;
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + i * 16 + fr;
+        af[i] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Ab + r * BK + 8 * (c ^ swz(r))));
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * (BN / WNG) + t * 16 + fr;
+        bfr[t] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Bb + r * BK + 8 * (c ^ swz(r))));
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
           acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
-
+  __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): the trailing reloads land before LDS is reused
+  __syncthreads();
+  // Epilogue from registers, as in k_gemm_tile.
+  const int colb = v0 + wn * (BN / WNG) + fr;
+  if (a.logits) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * (BM / 2) + i * 16 + 4 * fc + q;
+        if (m < M) {
+          float *dst = a.logits + (size_t)m * V;
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            if (colb + t * 16 < V) dst[colb + t * 16] = acc[i][t][q];
+        }
+      }
+  }
+  float *X = reinterpret_cast<float *>(S);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int t = 0; t < TN; ++t)
+    for (int q = 0; q < 4; ++q) {
+      float t1 = -INFINITY, t2 = -INFINITY;
+      int a1 = 0x7fffffff;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = wm * TM * 16 + i * 16 + 4 * (lane >> 4) + q;
-        const int cc = wn * TN * 16 + t * 16 + (lane & 15);
-        Cs[rr * LDC + cc] = acc[i][t][q];
+      for (int t = 0; t < TN; ++t) {
+        const int v = colb + t * 16;
+        const float z = acc[i][t][q];
+        if (v < V) {
+          if (beats(z, v, t1, a1)) { t2 = t1; t1 = z; a1 = v; }
+          else if (z > t2) t2 = z;
+        }
       }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+        const int oa = __shfl_xor(a1, off);
+        if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+        else { t2 = fmaxf(t2, o1); }
+      }
+      float s = 0.f;
+      if (a.scale_log2 > 0.f) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          if (colb + t * 16 < V) s += exp2f((acc[i][t][q] - t1) * a.scale_log2);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      }
+      if (fr == 0) {
+        const int rl = wm * (BM / 2) + i * 16 + 4 * fc + q;
+        float *x = X + (wn * BM + rl) * 4;   // [WNG][BM][4]
+        x[0] = t1; x[1] = t2; x[2] = __int_as_float(a1); x[3] = s;
+      }
+    }
   __syncthreads();
-  if (a.logits) tile_store_logits<BM, BN, LDC>(Cs, a.logits, m0, v0, M, V);
-  const RowAcc ts = tile_row_stats<BM, BN, LDC>(Cs, v0, V, a.scale_log2);
-  constexpr int TPR = 256 / BM;
-  const int m = m0 + tid / TPR;
-  if (tid % TPR == 0 && m < M) {
+  for (int rl = tid; rl < BM; rl += NT) {
+    const int m = m0 + rl;
+    if (m >= M) continue;
+    const float *x0 = X + rl * 4;
+    RowAcc r0{x0[0], x0[1], x0[3], __float_as_int(x0[2])};
+    for (int w = 1; w < WNG; ++w) {
+      const float *x1 = X + (w * BM + rl) * 4;
+      const RowAcc r1{x1[0], x1[1], x1[3], __float_as_int(x1[2])};
+      row_acc_merge(r0, r1, a.scale_log2);
+    }
     TilePartial p;
-    p.top1 = ts.t1; p.top2 = ts.t2; p.arg = ts.arg; p.sum = ts.sum;
-    a.partials[(size_t)m * a.part_stride + blockIdx.x] = p;
+    p.top1 = r0.t1; p.top2 = r0.t2; p.arg = r0.arg; p.sum = r0.sum;
+    a.partials[(size_t)m * a.part_stride + nt] = p;
   }
 }
 
@@ -524,12 +767,29 @@ hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
   if (cap <= 16) return launch_stream<1, 64, 256>(a, 0, stream);
   if (cap <= 32) return launch_stream<2, 64, 128>(a, 1, stream);
   if (cap <= 64) return launch_stream<4, 64, 128>(a, 2, stream);
-  constexpr int BM = 128, BN = 128;
-  const int nvt = (a.V + BN - 1) / BN;
-  hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(nvt, (cap + BM - 1) / BM), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_row_merge, dim3(cap), dim3(256), 0, stream, a, nvt);
+  constexpr int BM = 256;
+  const int n_mt = (cap + BM - 1) / BM;
+  hipError_t e;
+  int n_nt;
+  if (a.d % 64 == 0 && cap <= 1024) {        // a few hundred rows
+    constexpr int BN = 128;
+    n_nt = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 3, 8>), dim3(n_mt * n_nt), dim3(512), 0, stream, a, n_mt, n_nt);
+  } else if (a.d % 64 == 0) {                 // many rows: bound by the matrix cores
+    constexpr int BN = 256;
+    n_nt = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 2, 8>), dim3(n_mt * n_nt), dim3(512), 0, stream, a, n_mt, n_nt);
+  } else if (cap <= 1024) {  // general d (register-staged K loop with a K tail)
+    constexpr int BN = 128;
+    n_nt = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * n_nt), dim3(256), 0, stream, a, n_mt, n_nt);
+  } else {                  // many rows: bound by the matrix cores
+    constexpr int BN = 256;
+    n_nt = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * n_nt), dim3(256), 0, stream, a, n_mt, n_nt);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_row_merge, dim3(cap), dim3(256), 0, stream, a, n_nt);
   return hipGetLastError();
 }
 

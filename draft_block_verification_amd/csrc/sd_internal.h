@@ -127,12 +127,21 @@ hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_
                                 int32_t *accept_len, int32_t *next_token, int64_t *counters,
                                 hipStream_t stream);
 
+// Byte offsets inside the rejection-accept workspace.
+struct AcceptLayout {
+  int chunks;       // vocabulary chunks per row
+  size_t lse_q;     // double [B][gamma] drafter log-normalisers (right after the header)
+  size_t acc_a;     // int32 [B] accepted lengths
+  size_t dpart;     // drafter chunk partials [B][gamma][chunks]
+  size_t csum;      // double [B][chunks][2] draw-weight chunk sums
+};
+size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay);
+
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
                                    const uint16_t *draft_logits, const int32_t *draft_tokens,
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
-                                   int64_t *counters, double *lse_q, WsHeader *ws,
-                                   hipStream_t stream);
+                                   int64_t *counters, void *workspace, hipStream_t stream);
 
 }  // namespace sdv
