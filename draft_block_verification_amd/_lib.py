@@ -35,6 +35,8 @@ _SIGS = {
     "sd_truncate_by_confidence": (_i32, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
     "sd_verify_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                 _vp, _sz, _vp]),
+    "sd_verify_contraction": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
+                                     _vp]),
     "sd_accept_greedy": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sd_accept_rejection": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -177,6 +179,28 @@ def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
                                  _ptr(row_offsets), B, g, d, V, float(temperature), _ptr(logits),
                                  _ptr(stats), _ptr(workspace), workspace.numel(), _stream(stream)))
     return logits, stats
+
+
+def sd_verify_contraction(hidden: torch.Tensor, lm_head: torch.Tensor,
+                          verify_len: Optional[torch.Tensor] = None,
+                          row_offsets: Optional[torch.Tensor] = None, temperature: float = 0.0,
+                          logits: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """The contraction stage alone (logits and workspace partials, no row statistics)."""
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(lm_head, "lm_head", torch.bfloat16)
+    B, g1, d = hidden.shape
+    V = lm_head.shape[0]
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (B * g1, V))
+    if workspace is None:
+        workspace = new_workspace(verify_workspace_bytes(B, g1 - 1, d, V), hidden.device, stream)
+    _check("sd_verify_contraction",
+           _lib.sd_verify_contraction(_ptr(hidden), _ptr(lm_head), _ptr(verify_len),
+                                      _ptr(row_offsets), B, g1 - 1, d, V, float(temperature),
+                                      _ptr(logits), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return logits
 
 
 def sd_accept_greedy(stats: torch.Tensor, draft_tokens: torch.Tensor,

@@ -107,28 +107,30 @@ int32_t sd_truncate_by_confidence(const float *conf, int32_t B, int32_t gamma, f
                                        (hipStream_t)stream));
 }
 
-int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
-                         const int32_t *draft_tokens, const int32_t *verify_len,
-                         const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
-                         int32_t V, float temperature, float *logits, sd_row_stats *stats,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-  if (!hidden || !lm_head || !stats) return SD_EINVAL;
+namespace {
+
+// Shared validation and argument set-up of sd_verify_logits / sd_verify_contraction.
+int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head,
+                     const int32_t *draft_tokens, const int32_t *verify_len,
+                     const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d, int32_t V,
+                     float temperature, float *logits, sd_row_stats *stats, bool need_stats,
+                     void *workspace, size_t workspace_bytes, VerifyArgs *out) {
+  if (!hidden || !lm_head || (need_stats && !stats)) return SD_EINVAL;
   if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
   if (!isfinite(temperature) || temperature < 0.f) return SD_EINVAL;
   const int32_t sz = check_sizes(B, gamma, d, V);
   if (sz != SD_OK) return sz;
-  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || !aligned(stats, 8) ||
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || (stats && !aligned(stats, 8)) ||
       (logits && !aligned(logits, 16)) || (draft_tokens && !aligned(draft_tokens, 4)) ||
       (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
     return SD_EALIGN;
   if (!workspace || workspace_bytes < verify_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
-
   size_t part_off = 0;
   int part_stride = 0;
   verify_workspace_layout(B, gamma, V, &part_off, &part_stride);
   char *wsb = reinterpret_cast<char *>(workspace);
-  VerifyArgs a;
+  VerifyArgs &a = *out;
   a.hidden = hidden;
   a.W = lm_head;
   a.draft_tokens = draft_tokens;
@@ -144,7 +146,36 @@ int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
   a.part_stride = part_stride;
   a.stats = stats;
   a.ws = reinterpret_cast<WsHeader *>(workspace);
+  return SD_OK;
+}
+
+}  // namespace
+
+int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
+                         const int32_t *draft_tokens, const int32_t *verify_len,
+                         const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                         int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma,
+                                  d, V, temperature, logits, stats, true, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
   return launch_status(launch_verify(a, (hipStream_t)stream));
+}
+
+int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
+                              const int32_t *verify_len, const int32_t *row_offsets, int32_t B,
+                              int32_t gamma, int32_t d, int32_t V, float temperature,
+                              float *logits, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, nullptr, verify_len, row_offsets, B, gamma, d,
+                                  V, temperature, logits, nullptr, false, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  int n_part = 0;
+  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part));
 }
 
 int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,

@@ -722,7 +722,7 @@ struct Occupancy {
 Occupancy g_occ;
 
 template <int MT, int BN, int KC>
-hipError_t launch_stream(const VerifyArgs &a, int variant, hipStream_t stream) {
+hipError_t launch_stream(const VerifyArgs &a, int variant, hipStream_t stream, int *n_part) {
   if (g_occ.device < 0) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -744,10 +744,8 @@ hipError_t launch_stream(const VerifyArgs &a, int variant, hipStream_t stream) {
   const int g0 = min(nslab, min(resident, a.part_stride));
   const int rounds = (nslab + g0 - 1) / g0;
   const int G = (nslab + rounds - 1) / rounds;   // every workgroup gets rounds or rounds-1 slabs
+  *n_part = G;
   hipLaunchKernelGGL((k_gemm_stream<MT, BN, KC>), dim3(G), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, a, G);
   return hipGetLastError();
 }
 
@@ -762,34 +760,38 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
   return po + align_up(cap * (size_t)stride * sizeof(TilePartial), 256);
 }
 
-hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
+hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part) {
   const int cap = a.rm.B * (a.rm.gamma + 1);
-  if (cap <= 16) return launch_stream<1, 64, 256>(a, 0, stream);
-  if (cap <= 32) return launch_stream<2, 64, 128>(a, 1, stream);
-  if (cap <= 64) return launch_stream<4, 64, 128>(a, 2, stream);
+  if (cap <= 16) return launch_stream<1, 64, 256>(a, 0, stream, n_part);
+  if (cap <= 32) return launch_stream<2, 64, 128>(a, 1, stream, n_part);
+  if (cap <= 64) return launch_stream<4, 64, 128>(a, 2, stream, n_part);
   constexpr int BM = 256;
   const int n_mt = (cap + BM - 1) / BM;
-  hipError_t e;
-  int n_nt;
   if (a.d % 64 == 0 && cap <= 1024) {        // a few hundred rows
     constexpr int BN = 128;
-    n_nt = (a.V + BN - 1) / BN;
-    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 3, 8>), dim3(n_mt * n_nt), dim3(512), 0, stream, a, n_mt, n_nt);
+    *n_part = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 3, 8>), dim3(n_mt * *n_part), dim3(512), 0, stream, a, n_mt, *n_part);
   } else if (a.d % 64 == 0) {                 // many rows: bound by the matrix cores
     constexpr int BN = 256;
-    n_nt = (a.V + BN - 1) / BN;
-    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 2, 8>), dim3(n_mt * n_nt), dim3(512), 0, stream, a, n_mt, n_nt);
+    *n_part = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 2, 8>), dim3(n_mt * *n_part), dim3(512), 0, stream, a, n_mt, *n_part);
   } else if (cap <= 1024) {  // general d (register-staged K loop with a K tail)
     constexpr int BN = 128;
-    n_nt = (a.V + BN - 1) / BN;
-    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * n_nt), dim3(256), 0, stream, a, n_mt, n_nt);
-  } else {                  // many rows: bound by the matrix cores
+    *n_part = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * *n_part), dim3(256), 0, stream, a, n_mt, *n_part);
+  } else {
     constexpr int BN = 256;
-    n_nt = (a.V + BN - 1) / BN;
-    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * n_nt), dim3(256), 0, stream, a, n_mt, n_nt);
+    *n_part = (a.V + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * *n_part), dim3(256), 0, stream, a, n_mt, *n_part);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_row_merge, dim3(cap), dim3(256), 0, stream, a, n_nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
+  int n_part = 0;
+  hipError_t e = launch_contraction(a, stream, &n_part);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, a, n_part);
   return hipGetLastError();
 }
 

@@ -118,6 +118,8 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
 
 // Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
+// The contraction kernel alone; *n_part receives the partial columns written per row.
+hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part);
 
 hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
                            int32_t *verify_len, int32_t *row_offsets, hipStream_t stream);

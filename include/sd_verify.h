@@ -141,6 +141,20 @@ SD_API int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The LM-head contraction stage of sd_verify_logits on its own (same passages):
+ * writes the fp32 logits (when logits != NULL) and leaves per-row partial
+ * statistics in `workspace`; it does not produce sd_row_stats. It runs exactly the
+ * contraction kernel sd_verify_logits runs first, so it serves to time that kernel
+ * alone, and callers that only need the logits can use it. Arguments as for
+ * sd_verify_logits.
+ */
+SD_API int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
+                                     const int32_t *verify_len, const int32_t *row_offsets,
+                                     int32_t B, int32_t gamma, int32_t d, int32_t V,
+                                     float temperature, float *logits, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Greedy acceptance (LFM2.5-DSpark blog, "Quality parity"): a_r = first j < L_r
  * with stats[row_offsets[r] + j].argmax != draft_tokens[r][j], else L_r; the
  * emitted token is the target argmax of row a_r (a correction when a_r < L_r,
