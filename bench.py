@@ -59,7 +59,7 @@ def contraction_kernel(w) -> str:
     """Name of the kernel sd_verify_contraction launches for this shape."""
     cap = w.B * (w.gamma + 1)
     if cap <= 64:
-        return "k_gemm_stream"
+        return "k_gemm_skinny" if w.d % 128 == 0 else "k_gemm_stream"
     return "k_gemm_dma" if w.d % 64 == 0 else "k_gemm_tile"
 
 

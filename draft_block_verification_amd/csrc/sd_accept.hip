@@ -161,22 +161,23 @@ __device__ inline float block_max_f(float x, float *red) {
   return r;
 }
 
-// This thread's kPer drafter logits of chunk c (-inf past V).
+// kPer drafter logits of chunk c held by this thread: ids c*kChunk + 8*(tid + 256 h) + e
+// for h < kPer/8, e < 8 (each wave load is 1 KB contiguous); -inf past V.
 __device__ inline void load_draft_chunk(const uint16_t *row, int V, int c, float *x) {
-  const int v0 = c * kChunk + threadIdx.x * kPer;
-  if ((V & 7) == 0 && v0 + kPer <= V) {
 #pragma unroll
-    for (int h = 0; h < kPer / 8; ++h) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v0 + 8 * h);
+  for (int h = 0; h < kPer / 8; ++h) {
+    const int v0 = c * kChunk + 8 * (threadIdx.x + 256 * h);
+    if ((V & 7) == 0 && v0 + 8 <= V) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         x[8 * h + 2 * q] = __uint_as_float(w[q] << 16);
         x[8 * h + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) x[e] = v0 + e < V ? bf16_to_f32(row[v0 + e]) : -INFINITY;
+      for (int e = 0; e < 8; ++e) x[8 * h + e] = v0 + e < V ? bf16_to_f32(row[v0 + e]) : -INFINITY;
+    }
   }
 }
 
@@ -206,9 +207,14 @@ __global__ __launch_bounds__(256) void k_draft_partial(RejArgs a) {
   }
 }
 
+// One workgroup per request; 16 lanes per draft row (16 rows per pass). A row's
+// token, statistics, uniform and chunk partials are loaded together, the drafted
+// token's drafter logit as soon as its id is known.
+constexpr int kDecideHold = 4;   // chunk partials held per lane (C <= 64 without reloads)
+
 __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
   __shared__ int s_rej[64];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x, tid = threadIdx.x, sub = tid & 15;
   const int gamma = a.rm.gamma;
   const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
   const int base = request_base(a.rm, r, L, tid == 0 ? a.ws : nullptr);
@@ -216,45 +222,66 @@ __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
     if (tid == 0) { a.acc_a[r] = -1; a.accept_len[r] = 0; a.next_token[r] = -1; }
     return;
   }
-  for (int j = wave; j < L; j += 4) {
-    const DraftPart *P = a.dpart + ((size_t)r * gamma + j) * a.C;
-    float M = -INFINITY;
-    for (int c = lane; c < a.C; c += kWave) M = fmaxf(M, P[c].m);
+  for (int j0 = 0; j0 < L; j0 += 16) {
+    const int j = j0 + (tid >> 4);
+    const bool live = j < L;
+    const size_t rj = (size_t)r * gamma + (live ? j : 0);
+    const int x = live ? a.draft_tokens[rj] : -1;
+    const bool xok = x >= 0 && x < a.V;
+    double zx = 0.0, lse_p = 0.0;
+    float u = 1.f;
+    if (live && sub == 0) {
+      zx = a.stats[base + j].z_draft;
+      lse_p = a.stats[base + j].lse;
+      u = a.u_accept[rj];
+    }
+    const DraftPart *P = a.dpart + rj * a.C;
+    DraftPart hold[kDecideHold];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int i = 0; i < kDecideHold; ++i) {
+      const int c = sub + 16 * i;
+      hold[i] = live && c < a.C ? P[c] : DraftPart{-INFINITY, 0.f, 0.0};
+    }
+    const float lx = xok ? bf16_to_f32(a.draft_logits[rj * a.V + x]) : 0.f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kDecideHold; ++i) M = fmaxf(M, hold[i].m);
+    for (int c = sub + 16 * kDecideHold; live && c < a.C; c += 16) M = fmaxf(M, P[c].m);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     double S = 0.0;
-    for (int c = lane; c < a.C; c += kWave) {
+#pragma unroll
+    for (int i = 0; i < kDecideHold; ++i)
+      if (hold[i].s != 0.0) S += hold[i].s * exp(((double)hold[i].m - (double)M) * a.invT);
+    for (int c = sub + 16 * kDecideHold; live && c < a.C; c += 16) {
       const DraftPart q = P[c];
       if (q.s != 0.0) S += q.s * exp(((double)q.m - (double)M) * a.invT);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-    if (lane == 0) {
+    for (int off = 8; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    if (live && sub == 0) {
       const double lse = (double)M * a.invT + log(S);
-      a.lse_q[(size_t)r * gamma + j] = lse;
-      const int x = a.draft_tokens[(size_t)r * gamma + j];
+      a.lse_q[rj] = lse;
       int rej = 1;
-      if (x >= 0 && x < a.V) {
-        const sd_row_stats st = a.stats[base + j];
-        const double lx = (double)bf16_to_f32(a.draft_logits[((size_t)r * gamma + j) * a.V + x]);
-        const double logp = st.z_draft * a.invT - st.lse;
-        const double logq = lx * a.invT - lse;
-        const double ratio = exp(logp - logq);
-        rej = !((double)a.u_accept[(size_t)r * gamma + j] < fmin(1.0, ratio));
+      if (xok) {
+        const double logp = zx * a.invT - lse_p;
+        const double logq = (double)lx * a.invT - lse;
+        rej = !((double)u < fmin(1.0, exp(logp - logq)));
       }
       s_rej[j] = rej;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = L;
-    for (int j = 0; j < L; ++j)
-      if (s_rej[j]) { acc = j; break; }
-    a.acc_a[r] = acc;
-    a.accept_len[r] = acc;
-    if (a.counters) {
-      atomicAdd(reinterpret_cast<unsigned long long *>(a.counters), (unsigned long long)L);
-      atomicAdd(reinterpret_cast<unsigned long long *>(a.counters + 1), (unsigned long long)acc);
+  if (tid < 64) {
+    const unsigned long long m = __ballot(tid < L && s_rej[tid]);
+    if (tid == 0) {
+      const int acc = m ? (__ffsll((long long)m) - 1) : L;
+      a.acc_a[r] = acc;
+      a.accept_len[r] = acc;
+      if (a.counters) {
+        atomicAdd(reinterpret_cast<unsigned long long *>(a.counters), (unsigned long long)L);
+        atomicAdd(reinterpret_cast<unsigned long long *>(a.counters + 1), (unsigned long long)acc);
+      }
     }
   }
 }
@@ -295,20 +322,45 @@ __device__ inline void draw_weights(const DrawRow &d, int v, float *p, float *re
   }
 }
 
+// Chunk sums of the draw weights: ids c*kChunk + 4*(tid + 256 e) + i (16-byte logit
+// loads, each wave load 1 KB contiguous).
 __global__ __launch_bounds__(256) void k_draw_partial(RejArgs a) {
   __shared__ double red[4];
   const int r = blockIdx.y, c = blockIdx.x;
   DrawRow d;
   int arow;
   if (!draw_row(a, r, &d, &arow)) return;
-  const int v0 = c * kChunk + threadIdx.x * kPer;
   double sr = 0.0, sp = 0.0;
-  for (int e = 0; e < kPer; ++e) {
-    if (v0 + e < a.V) {
-      float p, w;
-      draw_weights(d, v0 + e, &p, &w);
-      sr += (double)w;
-      sp += (double)p;
+#pragma unroll
+  for (int e = 0; e < kPer / 4; ++e) {
+    const int v0 = c * kChunk + 4 * (threadIdx.x + 256 * e);
+    float z[4], ql[4];
+    if ((a.V & 3) == 0 && v0 + 4 <= a.V) {
+      const f32x4 zv = *reinterpret_cast<const f32x4 *>(d.z + v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = zv[i];
+      if (d.q) {
+        const uint2 qv = *reinterpret_cast<const uint2 *>(d.q + v0);
+        ql[0] = __uint_as_float(qv.x << 16); ql[1] = __uint_as_float(qv.x & 0xffff0000u);
+        ql[2] = __uint_as_float(qv.y << 16); ql[3] = __uint_as_float(qv.y & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = v0 + i < a.V;
+        z[i] = in ? d.z[v0 + i] : -INFINITY;
+        ql[i] = in && d.q ? bf16_to_f32(d.q[v0 + i]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (v0 + i < a.V) {
+        const float p = expf((float)((double)z[i] * d.invT - d.lse_p));
+        float w = p;
+        if (d.q) w = fmaxf(p - expf((float)((double)ql[i] * d.invT - d.lse_q)), 0.f);
+        sr += (double)w;
+        sp += (double)p;
+      }
     }
   }
   sr = block_sum_d(sr, red);
@@ -329,32 +381,68 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   const int gamma = a.rm.gamma;
   const int acc = a.acc_a[r];
   const double *cs = a.csum + (size_t)r * a.C * 2;
+  // Chunk sums in chunk order: thread t owns chunks t*K .. t*K + K - 1 (K = ceil(C/256)),
+  // an inclusive block scan gives every chunk's running sum.
+  int use_p = 0;
+  double S = 0.0, excl = 0.0, own = 0.0;
+  const int K = (a.C + 255) / 256, c0 = tid * K;
+  for (int pass = 0; pass < 2; ++pass) {
+    own = 0.0;
+    for (int k = 0; k < K; ++k)
+      if (c0 + k < a.C) own += cs[2 * (c0 + k) + use_p];
+    double incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_d[wave] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int q = 0; q < wave; ++q) before += s_d[q];
+    excl = before + (incl - own);
+    S = ((s_d[0] + s_d[1]) + s_d[2]) + s_d[3];
+    __syncthreads();
+    if (S != 0.0 || !d.q || pass == 1) break;
+    // No residual mass (p == q at this row): draw from p instead.
+    if (tid == 0) raise_flag(a.ws, SD_FLAG_NO_RESIDUAL);
+    use_p = 1;
+  }
+  const double thresh = (double)a.u_resample[(size_t)r * (gamma + 1) + acc] * S;
+  // First chunk whose running sum passes thresh; else (rounding) the last chunk with
+  // positive weight.
+  int first = 0x7fffffff, lastc = -1;
+  if (S > 0.0) {
+    double run = excl;
+    for (int k = 0; k < K && c0 + k < a.C; ++k) {
+      const double w = cs[2 * (c0 + k) + use_p];
+      if (first == 0x7fffffff && run + w > thresh) first = c0 + k;
+      run += w;
+      if (w > 0.0) lastc = c0 + k;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    first = min(first, __shfl_xor(first, off));
+    lastc = max(lastc, __shfl_xor(lastc, off));
+  }
+  if (lane == 0) { s_i[4 + wave] = first; s_i[8 + wave] = lastc; }
+  __syncthreads();
   if (tid == 0) {
-    int col = 0;
-    double S = 0.0;
-    for (int c = 0; c < a.C; ++c) S += cs[2 * c];
-    if (S == 0.0 && d.q) {            // no residual mass (p == q at this row): draw from p
-      raise_flag(a.ws, SD_FLAG_NO_RESIDUAL);
-      col = 1;
-      S = 0.0;
-      for (int c = 0; c < a.C; ++c) S += cs[2 * c + 1];
+    int f = s_i[4], l = s_i[8];
+    for (int q = 1; q < 4; ++q) { f = min(f, s_i[4 + q]); l = max(l, s_i[8 + q]); }
+    const int hit = f != 0x7fffffff ? f : l;
+    s_i[0] = hit; s_i[1] = f == 0x7fffffff ? 1 : 0; s_i[2] = use_p;
+  }
+  // Running sum before the hit chunk: the owner thread of that chunk knows it.
+  __syncthreads();
+  {
+    const int h = s_i[0];
+    if (h >= 0 && h >= c0 && h < c0 + K) {
+      double run = excl;
+      for (int c = c0; c < h; ++c) run += cs[2 * c + use_p];
+      s_d[0] = run;
     }
-    const double thresh = (double)a.u_resample[(size_t)r * (gamma + 1) + acc] * S;
-    int hit = -1, last_pos = 0;
-    double carry = 0.0;
-    if (S > 0.0) {
-      for (int c = 0; c < a.C; ++c) {
-        if (carry + cs[2 * c + col] > thresh) { hit = c; break; }
-        carry += cs[2 * c + col];
-      }
-      if (hit < 0) {                  // rounding: the last id with positive weight
-        last_pos = 1;
-        for (int c = a.C - 1; c >= 0; --c)
-          if (cs[2 * c + col] > 0.0) { hit = c; break; }
-      }
-    }
-    s_i[0] = hit; s_i[1] = last_pos; s_i[2] = col;
-    s_d[0] = carry; s_d[1] = thresh;
   }
   __syncthreads();
   const int hit = s_i[0], last_pos = s_i[1], col = s_i[2];
@@ -363,18 +451,40 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
     return;
   }
   if (col == 1) d.q = nullptr;
-  const double carry = s_d[0], thresh = s_d[1];
+  const double carry = s_d[0];
   // Scan the crossing chunk: kPer consecutive ids per thread, exclusive scan of the
   // per-thread sums, then the crossing thread walks its ids.
   const int v0 = hit * kChunk + tid * kPer;
   float w[kPer];
   double mine = 0.0;
-  for (int e = 0; e < kPer; ++e) {
-    float p = 0.f, x = 0.f;
-    if (v0 + e < a.V) draw_weights(d, v0 + e, &p, &x);
-    w[e] = x;
-    mine += (double)x;
+  if ((a.V & 7) == 0 && v0 + kPer <= a.V) {
+#pragma unroll
+    for (int h = 0; h < kPer / 4; ++h) {
+      const f32x4 zv = *reinterpret_cast<const f32x4 *>(d.z + v0 + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[4 * h + i] = expf((float)((double)zv[i] * d.invT - d.lse_p));
+    }
+    if (d.q) {
+#pragma unroll
+      for (int h = 0; h < kPer / 8; ++h) {
+        const u32x4 qv = *reinterpret_cast<const u32x4 *>(d.q + v0 + 8 * h);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float ql = __uint_as_float((i & 1) ? (qv[i >> 1] & 0xffff0000u) : (qv[i >> 1] << 16));
+          w[8 * h + i] = fmaxf(w[8 * h + i] - expf((float)((double)ql * d.invT - d.lse_q)), 0.f);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      float p = 0.f, x = 0.f;
+      if (v0 + e < a.V) draw_weights(d, v0 + e, &p, &x);
+      w[e] = x;
+    }
   }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) mine += (double)w[e];
   double incl = mine;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {

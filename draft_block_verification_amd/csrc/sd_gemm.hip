@@ -7,22 +7,36 @@
 // flattened rather than padded).
 //
 // Both operands are K-contiguous bf16 (hidden rows [M][d], LM head [V][d]); products
-// run on the 16x16x32 bf16 MFMA with fp32 accumulation. Two regimes:
-//   * streaming (M <= 64), k_gemm_stream: a persistent grid walks the vocabulary in
-//     slabs of BN rows. Each stage moves KC k-values of the slab and of the hidden
-//     rows into LDS with contiguous 512-byte row segments per wave load (W is read
-//     from HBM exactly once); the LDS layout XORs each row's 16-byte chunk index
-//     with (row & 15) so MFMA fragment reads from 16 rows hit 16 bank groups. Per
-//     slab the fp32 tile is reduced to row statistics and merged into running
-//     values, leaving one partial per (row, workgroup).
-//   * tiled (M > 64), k_gemm_tile: BM x BN output tiles staged through LDS, one
-//     partial per (row, vocabulary tile).
+// run on the 16x16x32 bf16 MFMA with fp32 accumulation. Regimes by row capacity:
+//   * streaming (M <= 64): a persistent grid walks the vocabulary in 64-row slabs and
+//     reads W from HBM exactly once. k_gemm_skinny (d % 128 == 0) moves each stage
+//     straight into LDS with global_load_lds and keeps NS-1 stages in flight;
+//     k_gemm_stream (any d % 8 == 0) stages through registers. One partial per
+//     (row, workgroup).
+//   * tiled (M > 64): BM x BN output tiles, k_gemm_dma (direct-to-LDS, 8 waves, for
+//     d % 64 == 0) or k_gemm_tile (register-staged, any d); one partial per (row,
+//     vocabulary tile).
 // k_row_merge then combines each row's partials (one workgroup per row).
 // Row statistics: max, second max, lowest argmax and sum of exp((z - max) / T); the
 // drafted token's logit is recomputed exactly as an fp64 dot of the bf16 inputs.
 #include <math.h>
 
 #include "sd_internal.h"
+
+#define LDSP __attribute__((address_space(3)))
+#define GLBP __attribute__((address_space(1)))
+
+// Cache-policy operand of global_load_lds for data read exactly once (the nt bit).
+constexpr int kCachePolicyStream = 2;
+
+// Workgroup barrier without the vmcnt(0) that __syncthreads implies: callers wait for
+// their own direct-to-LDS loads with an explicit vmcnt first. The empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 namespace sdv {
 namespace {
@@ -114,32 +128,6 @@ __device__ inline double block_sum(double x, double *red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   return ((red[0] + red[1]) + red[2]) + red[3];
-}
-
-// Exact logit of row m's drafted token: an fp64 dot of the bf16 hidden row and LM-head
-// row (bf16 x bf16 products are exact in fp64). 0 on bonus rows. All 256 threads call it.
-__device__ double drafted_logit(const VerifyArgs &a, int m, double *red) {
-  int r, j;
-  const int hr = hidden_row(a.rm, m, &r, &j);
-  int x = -1;
-  if (hr >= 0 && a.draft_tokens &&
-      j < clamp_len(a.verify_len, r, a.rm.gamma, threadIdx.x == 0 ? a.ws : nullptr))
-    x = a.draft_tokens[(size_t)r * a.rm.gamma + j];
-  if (x < 0 || x >= a.V) return 0.0;           // uniform across the workgroup
-  const uint16_t *h = a.hidden + (size_t)hr * a.d;
-  const uint16_t *w = a.W + (size_t)x * a.d;
-  double part = 0.0;
-  for (int c = threadIdx.x; c < a.d / 8; c += 256) {
-    const u32x4 hv = *reinterpret_cast<const u32x4 *>(h + 8 * c);
-    const u32x4 wv = *reinterpret_cast<const u32x4 *>(w + 8 * c);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      part += (double)__uint_as_float(hv[q] << 16) * (double)__uint_as_float(wv[q] << 16);
-      part += (double)__uint_as_float(hv[q] & 0xffff0000u) *
-              (double)__uint_as_float(wv[q] & 0xffff0000u);
-    }
-  }
-  return block_sum(part, red);
 }
 
 __device__ inline void write_stats(const VerifyArgs &a, int m, float t1, float t2, int arg,
@@ -283,6 +271,173 @@ __global__ __launch_bounds__(256) void k_gemm_stream(VerifyArgs a) {
     TilePartial p;
     p.top1 = run.t1; p.top2 = run.t2; p.arg = run.arg; p.sum = run.sum;
     a.partials[(size_t)m * a.part_stride + g] = p;
+  }
+}
+
+// ------------------------------------------------- streaming regime, direct to LDS
+// The streaming kernel for d % KC == 0. global_load_lds_dwordx4 moves every wave
+// load's 1 KB (four 256-byte row segments for KC = 128) straight into one of NS LDS
+// stage buffers, so NS-1 stages stay in flight per workgroup with no registers held.
+// Wave w owns LM-head rows 16w..16w+15 of each 64-row slab over the full k range, so
+// a slab's 16 x 16 output tiles are complete in registers and its row statistics are
+// reduced with lane shuffles (no LDS round trip, no k-split reduction). A stage row
+// holds KC/8 16-byte chunks; chunk j of row r holds logical chunk j ^ (r & 15).
+// LM-head loads carry the streaming (non-temporal) cache policy: every byte is used
+// once. Workgroup g walks the k stages of a slab starting at stage (g * kstride) mod
+// nst (kstride coprime to nst), so concurrent workgroups read different offsets of
+// their rows instead of all hitting the same column of power-of-two-strided rows.
+template <int MT, int KC, int NS>
+__global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) {
+  constexpr int BN = 64;
+  constexpr int CH = KC / 8;                 // 16-byte chunks per stage row
+  constexpr int RPI = 64 / CH;               // stage rows per wave instruction
+  constexpr int ROWS = BN + 16 * MT;         // LM-head rows, then hidden rows
+  constexpr int STAGE = ROWS * KC;           // bf16 per stage buffer
+  constexpr int DPT = ROWS * CH / 256;       // wave instructions per wave per stage
+  constexpr int PEND = (NS - 2) * DPT;       // loads allowed in flight past the oldest stage
+  static_assert(CH >= 16 && CH <= 64 && ROWS % (4 * RPI) == 0, "stage shape");
+  static_assert(PEND < 64, "vmcnt holds 6 bits");
+  __shared__ __attribute__((aligned(16))) uint16_t S[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int M = rows_total(a.rm);
+  const int d = a.d, V = a.V;
+
+  // Load i of this thread fills stage row r = RPI * (wave + 4 i) + lane / CH, stored
+  // chunk lane % CH. The first WI loads cover the LM-head rows (they move with the
+  // slab), the rest the hidden rows (fixed source).
+  constexpr int WI = BN / (4 * RPI);
+  static_assert(BN % (4 * RPI) == 0, "LM-head rows fill whole loads");
+  int w_row[WI], w_chunk[WI];
+  const uint16_t *h_src[DPT - WI];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    const int r = RPI * (wave + 4 * i) + lane / CH;
+    const int chunk = 8 * ((lane % CH) ^ (r & 15));
+    if (i < WI) {
+      w_row[i] = r;
+      w_chunk[i] = chunk;
+    } else {
+      const int m = r - BN;
+      const uint16_t *src = a.hidden + chunk;   // rows past M read row 0; never used
+      if (m < M) {
+        int rq, jj;
+        const int hr = hidden_row(a.rm, m, &rq, &jj);
+        if (hr >= 0) src += (size_t)hr * d;
+        else raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      }
+      h_src[i - WI] = src;
+    }
+  }
+
+  const int nslab = (V + BN - 1) / BN;
+  const int nst = d / KC;
+  const int total = ((nslab - g + G - 1) / G) * nst;   // (slab, stage) pairs of this workgroup
+  const int kshift = (int)(((long long)g * kstride) % nst);
+  auto issue = [&](int t) {
+    const int slab = g + (t / nst) * G, k0 = ((t + kshift) % nst) * KC;
+    LDSP uint16_t *dst = (LDSP uint16_t *)S + (t % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      if (i < WI)
+        __builtin_amdgcn_global_load_lds(
+            (const GLBP void *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_chunk[i] + k0),
+            (LDSP void *)(dst + (wave + 4 * i) * 512), 16, 0, kCachePolicyStream);
+      else
+        __builtin_amdgcn_global_load_lds((const GLBP void *)(h_src[i - WI] + k0),
+                                         (LDSP void *)(dst + (wave + 4 * i) * 512), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  RowAcc run[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) run[i][q] = row_acc_init();
+  const int fr = lane & 15, fc = lane >> 4;
+  const int br = 16 * wave + fr;
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < total) issue(p);
+  for (int t = 0; t < total; ++t) {
+    // Stage t is complete once at most PEND newer loads of this thread are pending;
+    // in the last NS-2 pairs fewer loads follow it, so wait for all of them.
+    if (t + NS - 2 < total) {
+      __builtin_amdgcn_s_waitcnt((PEND & 15) | (((PEND >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    lds_barrier();
+    if (t + NS - 1 < total) issue(t + NS - 1);   // refills the buffer read in pair t - 1
+    const LDSP uint16_t *Sb = (const LDSP uint16_t *)S + (t % NS) * STAGE;
+#pragma unroll
+    for (int s = 0; s < KC / 32; ++s) {
+      const int c = 4 * s + fc;
+      const bf16x8 b = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + br * KC + 8 * (c ^ (br & 15))));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int ar = BN + 16 * i + fr;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + ar * KC + 8 * (c ^ (ar & 15))));
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[i], 0, 0, 0);
+      }
+    }
+    if (t % nst == nst - 1) {
+      // Slab done. Lane l holds rows 16 i + 4 (l >> 4) + q, vocabulary id v; reduce
+      // over the 16 lanes that share l >> 4.
+      const int v = (g + (t / nst) * G) * BN + br;
+      const bool vok = v < V;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float z = acc[i][q];
+          const int m = 16 * i + 4 * fc + q;
+          if (a.logits && vok && m < M) a.logits[(size_t)m * V + v] = z;
+          float t1 = vok ? z : -INFINITY, t2 = -INFINITY;
+          int a1 = vok ? v : 0x7fffffff;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+            const int oa = __shfl_xor(a1, off);
+            if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+            else { t2 = fmaxf(t2, o1); }
+          }
+          float s = 0.f;
+          if (a.scale_log2 > 0.f) {
+            s = vok ? exp2f((z - t1) * a.scale_log2) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
+          }
+          row_acc_merge(run[i][q], RowAcc{t1, t2, s, a1}, a.scale_log2);
+        }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Merge the four waves' running statistics in a fixed order; one partial per
+  // (row, workgroup). Every load into LDS has landed (the last pairs waited for all).
+  __syncthreads();
+  RowAcc *X = reinterpret_cast<RowAcc *>(S);   // [4][16 MT]
+  if (fr == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) X[wave * 16 * MT + 16 * i + 4 * fc + q] = run[i][q];
+  }
+  __syncthreads();
+  if (tid < 16 * MT && tid < M) {
+    RowAcc r0 = X[tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) row_acc_merge(r0, X[w * 16 * MT + tid], a.scale_log2);
+    TilePartial p;
+    p.top1 = r0.t1; p.top2 = r0.t2; p.arg = r0.arg; p.sum = r0.sum;
+    a.partials[(size_t)tid * a.part_stride + g] = p;
   }
 }
 
@@ -494,8 +649,6 @@ __global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a, int n_mt, int n
 // two waves per SIMD, which hides LDS read latency behind the other wave's MFMAs.
 // Rows of a stage are BK/8 16-byte chunks; chunk j of row r holds logical chunk
 // j ^ swz(r), so the MFMA fragment reads of 16 rows spread over the bank groups.
-#define LDSP __attribute__((address_space(3)))
-#define GLBP __attribute__((address_space(1)))
 template <int BM, int BN, int BK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, int n_nt) {
   constexpr int NT = 64 * NW;                      // threads
@@ -562,7 +715,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
     // Stage kt is complete once at most (NS-2)*DPT newer DMAs of this thread are pending.
     constexpr int PEND = (NS - 2) * DPT;
     __builtin_amdgcn_s_waitcnt((PEND & 15) | (((PEND >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     issue(kt + NS - 1);          // refills the buffer read in the previous iteration
     const LDSP uint16_t *Ab = (const LDSP uint16_t *)S + (kt % NS) * STAGE;
     const LDSP uint16_t *Bb = Ab + BM * BK;
@@ -660,8 +813,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
 }
 
 // One workgroup per verified row: merge the row's partials (loaded in one round of
-// independent loads, kMergePer per thread) and compute the exact drafted-token logit.
+// independent loads, kMergePer per thread) and compute the drafted token's exact logit,
+// an fp64 dot of the bf16 hidden and LM-head rows (bf16 x bf16 products are exact in
+// fp64). The hidden row is loaded before the partials, the LM-head row as soon as the
+// drafted token id is known, so the three memory round trips overlap.
 constexpr int kMergePer = 16;   // partials per thread per round (n <= 4096 in one round)
+constexpr int kDotPer = 4;      // 16-byte chunks per thread held for the dot (d <= 8192)
 
 __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   __shared__ double red[4];
@@ -671,11 +828,28 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   const int M = rows_total(a.rm);
   if (m >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = a.d / 8;
+
+  int r, j;
+  const int hr = hidden_row(a.rm, m, &r, &j);
+  const uint16_t *hrow = a.hidden + (size_t)(hr >= 0 ? hr : 0) * a.d;
+  int x = -1;
+  if (hr >= 0 && a.draft_tokens &&
+      j < clamp_len(a.verify_len, r, a.rm.gamma, tid == 0 ? a.ws : nullptr))
+    x = a.draft_tokens[(size_t)r * a.rm.gamma + j];
+  const bool has_x = x >= 0 && x < a.V;        // uniform across the workgroup
+  u32x4 hv[kDotPer];
+#pragma unroll
+  for (int i = 0; i < kDotPer; ++i) {
+    const int c = tid + 256 * i;
+    hv[i] = has_x && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+
   const TilePartial *P = a.partials + (size_t)m * a.part_stride;
   float t1 = -INFINITY, t2 = -INFINITY;
   int a1 = 0x7fffffff;
+  TilePartial q[kMergePer];
   for (int base = 0; base < n; base += 256 * kMergePer) {
-    TilePartial q[kMergePer];
 #pragma unroll
     for (int i = 0; i < kMergePer; ++i) {
       const int p = base + tid + 256 * i;
@@ -687,6 +861,14 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
       else { t2 = fmaxf(t2, q[i].top1); }
     }
   }
+  const uint16_t *wrow = a.W + (size_t)(has_x ? x : 0) * a.d;
+  u32x4 wv[kDotPer];
+#pragma unroll
+  for (int i = 0; i < kDotPer; ++i) {
+    const int c = tid + 256 * i;
+    wv[i] = has_x && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
@@ -704,25 +886,47 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   double lse = 0.0;
   if (a.temperature > 0.f) {
     double S = 0.0;
-    for (int p = tid; p < n; p += 256) {      // second pass hits the cache
-      const TilePartial q = P[p];
-      if (q.sum != 0.f) S += (double)q.sum * exp(((double)q.top1 - (double)t1) * a.invT);
+    if (n <= 256 * kMergePer) {               // this thread's partials are still in q
+#pragma unroll
+      for (int i = 0; i < kMergePer; ++i)
+        if (q[i].sum != 0.f) S += (double)q[i].sum * exp(((double)q[i].top1 - (double)t1) * a.invT);
+    } else {
+      for (int p = tid; p < n; p += 256) {
+        const TilePartial o = P[p];
+        if (o.sum != 0.f) S += (double)o.sum * exp(((double)o.top1 - (double)t1) * a.invT);
+      }
     }
     S = block_sum(S, red);
     lse = (double)t1 * a.invT + log(S);
   }
-  const double zd = drafted_logit(a, m, red);
+  double zd = 0.0;
+  if (has_x) {
+    double part = 0.0;
+    auto dot8 = [&](const u32x4 &h, const u32x4 &w) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part += (double)__uint_as_float(h[e] << 16) * (double)__uint_as_float(w[e] << 16);
+        part += (double)__uint_as_float(h[e] & 0xffff0000u) * (double)__uint_as_float(w[e] & 0xffff0000u);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kDotPer; ++i) dot8(hv[i], wv[i]);
+    for (int c = tid + 256 * kDotPer; c < nc; c += 256)
+      dot8(*reinterpret_cast<const u32x4 *>(hrow + 8 * c), *reinterpret_cast<const u32x4 *>(wrow + 8 * c));
+    zd = block_sum(part, red);
+  }
   if (tid == 0) write_stats(a, m, t1, t2, a1, lse, zd);
 }
 
-// Resident workgroups per CU for the streaming variants, cached for the current device.
+// Resident workgroups per CU of each persistent kernel, cached for the current device.
 struct Occupancy {
-  int device = -1, cus = 0, per_cu[3] = {0, 0, 0};
+  int device = -1, cus = 0;
+  const void *fn[8] = {};
+  int per_cu[8] = {};
 };
 Occupancy g_occ;
 
-template <int MT, int BN, int KC>
-hipError_t launch_stream(const VerifyArgs &a, int variant, hipStream_t stream, int *n_part) {
+int resident_blocks(const void *fn) {
   if (g_occ.device < 0) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -731,21 +935,50 @@ hipError_t launch_stream(const VerifyArgs &a, int variant, hipStream_t stream, i
     g_occ.cus = cus > 0 ? cus : 1;
     g_occ.device = dev;
   }
-  if (g_occ.per_cu[variant] == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_stream<MT, BN, KC>, 256, 0) !=
-        hipSuccess)
-      n = 1;
-    g_occ.per_cu[variant] = n > 0 ? n : 1;
-  }
-  const int nslab = (a.V + BN - 1) / BN;
-  const int resident = g_occ.cus * g_occ.per_cu[variant];
-  // At most one workgroup per resident slot and per partial column.
-  const int g0 = min(nslab, min(resident, a.part_stride));
+  int slot = 0;
+  while (slot < 8 && g_occ.fn[slot] && g_occ.fn[slot] != fn) ++slot;
+  if (slot < 8 && g_occ.fn[slot] == fn) return g_occ.cus * g_occ.per_cu[slot];
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess || n < 1) n = 1;
+  if (slot < 8) { g_occ.fn[slot] = fn; g_occ.per_cu[slot] = n; }
+  return g_occ.cus * n;
+}
+
+// Balanced persistent grid over BN-row slabs: at most one workgroup per resident slot
+// and per partial column, and every workgroup gets `rounds` or `rounds - 1` slabs.
+int persistent_grid(int nslab, int resident, int part_stride) {
+  const int g0 = min(nslab, min(resident, part_stride));
   const int rounds = (nslab + g0 - 1) / g0;
-  const int G = (nslab + rounds - 1) / rounds;   // every workgroup gets rounds or rounds-1 slabs
+  return (nslab + rounds - 1) / rounds;
+}
+
+template <int MT, int BN, int KC>
+hipError_t launch_stream(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+  const void *fn = reinterpret_cast<const void *>(&k_gemm_stream<MT, BN, KC>);
+  const int G = persistent_grid((a.V + BN - 1) / BN, resident_blocks(fn), a.part_stride);
   *n_part = G;
   hipLaunchKernelGGL((k_gemm_stream<MT, BN, KC>), dim3(G), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Smallest of a few small odd strides that is coprime to the stage count, so the
+// start offsets of consecutive workgroups cover every stage evenly.
+int stage_stride(int nst) {
+  for (int s : {5, 7, 11, 13, 3}) {
+    int x = nst, y = s;
+    while (y) { const int t = x % y; x = y; y = t; }
+    if (x == 1) return s;
+  }
+  return 1;
+}
+
+template <int MT, int KC, int NS>
+hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+  const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS>);
+  const int G = persistent_grid((a.V + 63) / 64, resident_blocks(fn), a.part_stride);
+  *n_part = G;
+  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS>), dim3(G), dim3(256), 0, stream, a,
+                     stage_stride(a.d / KC));
   return hipGetLastError();
 }
 
@@ -762,9 +995,14 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
 
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part) {
   const int cap = a.rm.B * (a.rm.gamma + 1);
-  if (cap <= 16) return launch_stream<1, 64, 256>(a, 0, stream, n_part);
-  if (cap <= 32) return launch_stream<2, 64, 128>(a, 1, stream, n_part);
-  if (cap <= 64) return launch_stream<4, 64, 128>(a, 2, stream, n_part);
+  if (a.d % 128 == 0) {
+    if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part);
+    if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part);
+    if (cap <= 64) return launch_skinny<4, 128, 2>(a, stream, n_part);
+  }
+  if (cap <= 16) return launch_stream<1, 64, 256>(a, stream, n_part);
+  if (cap <= 32) return launch_stream<2, 64, 128>(a, stream, n_part);
+  if (cap <= 64) return launch_stream<4, 64, 128>(a, stream, n_part);
   constexpr int BM = 256;
   const int n_mt = (cap + BM - 1) / BM;
   if (a.d % 64 == 0 && cap <= 1024) {        // a few hundred rows

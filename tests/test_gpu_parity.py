@@ -58,9 +58,12 @@ def full_case(w, steps, seed=0, check_all_logits=True):
 # ---------------------------------------------------------------- small shapes
 
 SHAPES = [
-    # (name, B, gamma, d, V, T, truncate): skinny 16/32/64-row tiles, LDS-tiled
-    # path, a K tail (d % 32 != 0), vocabulary tails (V % 64 != 0, V % 8 != 0).
+    # (name, B, gamma, d, V, T, truncate): skinny 16/32/64-row tiles (direct-to-LDS
+    # when d % 128 == 0, register-staged otherwise), LDS-tiled path, a K tail
+    # (d % 32 != 0), vocabulary tails (V % 64 != 0, V % 8 != 0).
     ("skinny16-greedy", 1, 4, 256, 1000, 0.0, False),
+    ("skinny32-dma-rej", 1, 20, 384, 2000, 1.0, False),
+    ("skinny64-dma-trunc", 3, 16, 512, 3001, 0.8, True),
     ("skinny16-rej", 2, 5, 40, 1001, 1.0, False),
     ("skinny32-rej", 1, 16, 264, 3000, 0.7, False),
     ("skinny64-trunc", 3, 16, 128, 777, 1.3, True),
