@@ -37,6 +37,8 @@ _SIGS = {
                                 _vp, _sz, _vp]),
     "sd_verify_contraction": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
                                      _vp]),
+    "sd_verify_greedy": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]),
     "sd_accept_greedy": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sd_accept_rejection": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -203,6 +205,46 @@ def sd_verify_contraction(hidden: torch.Tensor, lm_head: torch.Tensor,
     return logits
 
 
+def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: torch.Tensor,
+                     verify_len: Optional[torch.Tensor] = None,
+                     row_offsets: Optional[torch.Tensor] = None,
+                     stats: Optional[torch.Tensor] = None,
+                     accept_len: Optional[torch.Tensor] = None,
+                     next_token: Optional[torch.Tensor] = None,
+                     counters: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """Greedy verify in one call: returns (stats, accept_len, next_token)."""
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(lm_head, "lm_head", torch.bfloat16)
+    B, g1, d = hidden.shape
+    g = g1 - 1
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != d:
+        raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+    dev = hidden.device
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
+    if verify_len is not None:
+        _need(verify_len, "verify_len", torch.int32, (B,))
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    stats = new_stats(B, g, dev) if stats is None else stats
+    _need(stats, "stats", torch.int64, (B * g1, 4))
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _need(next_token, "next_token", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    if workspace is None:
+        workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
+    _check("sd_verify_greedy",
+           _lib.sd_verify_greedy(_ptr(hidden), _ptr(lm_head), _ptr(draft_tokens), _ptr(verify_len),
+                                 _ptr(row_offsets), B, g, d, V, _ptr(stats), _ptr(accept_len),
+                                 _ptr(next_token), _ptr(counters), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return stats, accept_len, next_token
+
+
 def sd_accept_greedy(stats: torch.Tensor, draft_tokens: torch.Tensor,
                      verify_len: Optional[torch.Tensor] = None,
                      row_offsets: Optional[torch.Tensor] = None,
@@ -265,12 +307,16 @@ class VerifyRound:
     """Buffers for repeated verify rounds of one shape; each run() enqueues the whole path.
 
     truncate -> verify logits -> accept (greedy when temperature == 0, else rejection),
-    all on one stream with no host synchronisation.
+    all on one stream with no host synchronisation. At temperature 0 the verify and
+    accept steps run through sd_verify_greedy (one launch fewer); fused=False keeps
+    the separate sd_verify_logits + sd_accept_greedy calls.
     """
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
-                 truncate: bool, threshold: float = 0.3, device="cuda", stream=None):
+                 truncate: bool, threshold: float = 0.3, device="cuda", stream=None,
+                 fused: bool = True):
         self.B, self.gamma, self.d, self.V = B, gamma, d, V
+        self.fused = fused
         self.T, self.truncate, self.threshold = float(temperature), truncate, float(threshold)
         dev = torch.device(device)
         rows = B * (gamma + 1)
@@ -291,6 +337,11 @@ class VerifyRound:
         if self.truncate:
             sd_truncate_by_confidence(conf, self.threshold, self.verify_len, self.row_offsets,
                                       stream=stream)
+        if self.T == 0 and self.fused:
+            sd_verify_greedy(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
+                             self.stats, self.accept_len, self.next_token, self.counters,
+                             self.ws_verify, stream=stream)
+            return self.accept_len, self.next_token
         sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                          self.T, self.logits, self.stats, self.ws_verify, stream=stream)
         if self.T > 0:

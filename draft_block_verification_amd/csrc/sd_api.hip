@@ -178,6 +178,23 @@ int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
   return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part));
 }
 
+int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
+                         const int32_t *draft_tokens, const int32_t *verify_len,
+                         const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                         int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                         int32_t *next_token, int64_t *counters, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  if (!draft_tokens || !accept_len || !next_token) return SD_EINVAL;
+  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
+    return SD_EALIGN;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma,
+                                  d, V, 0.f, nullptr, stats, true, workspace, workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
+                                            (hipStream_t)stream));
+}
+
 int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
                          const int32_t *verify_len, const int32_t *row_offsets, int32_t B,
                          int32_t gamma, int32_t *accept_len, int32_t *next_token,

@@ -918,6 +918,109 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   if (tid == 0) write_stats(a, m, t1, t2, a1, lse, zd);
 }
 
+// Greedy verify tail in one kernel: one workgroup per request merges the partials of
+// its rows 0..L_r (one wave per row), writes their statistics with the drafted
+// token's exact logit, then finds the first row whose argmax differs from the draft
+// and emits that row's argmax (LFM2.5-DSpark blog, "Quality parity").
+constexpr int kFusedWaves = 16;
+constexpr int kFusedPer = 8;    // loads in flight per lane
+
+__global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
+    VerifyArgs a, int n, int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
+    int64_t *__restrict__ counters) {
+  __shared__ int s_arg[65];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gamma = a.rm.gamma;
+  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  const int cap = a.rm.B * (gamma + 1);
+  const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
+  if (base < 0 || base + L >= cap) {
+    if (tid == 0) {
+      raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      accept_len[r] = 0;
+      next_token[r] = -1;
+    }
+    return;
+  }
+  const int nc = a.d / 8;
+  for (int j = wave; j <= L; j += kFusedWaves) {
+    const int m = base + j;
+    const int x = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
+    const bool has_x = x >= 0 && x < a.V;
+    const TilePartial *P = a.partials + (size_t)m * a.part_stride;
+    float t1 = -INFINITY, t2 = -INFINITY;
+    int a1 = 0x7fffffff;
+    for (int p0 = 0; p0 < n; p0 += 64 * kFusedPer) {
+      TilePartial q[kFusedPer];
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i) {
+        const int p = p0 + lane + 64 * i;
+        q[i] = p < n ? P[p] : TilePartial{-INFINITY, -INFINITY, 0x7fffffff, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i) {
+        if (beats(q[i].top1, q[i].arg, t1, a1)) { t2 = fmaxf(t1, q[i].top2); t1 = q[i].top1; a1 = q[i].arg; }
+        else { t2 = fmaxf(t2, q[i].top1); }
+      }
+    }
+    double part = 0.0;
+    if (has_x) {
+      const uint16_t *h = a.hidden + ((size_t)r * (gamma + 1) + j) * a.d;
+      const uint16_t *w = a.W + (size_t)x * a.d;
+      for (int c0 = 0; c0 < nc; c0 += 64 * kFusedPer) {
+        u32x4 hv[kFusedPer], wv[kFusedPer];
+#pragma unroll
+        for (int i = 0; i < kFusedPer; ++i) {
+          const int c = c0 + lane + 64 * i;
+          hv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(h + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+          wv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(w + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kFusedPer; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part += (double)__uint_as_float(hv[i][e] << 16) * (double)__uint_as_float(wv[i][e] << 16);
+            part += (double)__uint_as_float(hv[i][e] & 0xffff0000u) *
+                    (double)__uint_as_float(wv[i][e] & 0xffff0000u);
+          }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+      const int oa = __shfl_xor(a1, off);
+      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+      else { t2 = fmaxf(t2, o1); }
+      part += __shfl_xor(part, off);
+    }
+    if (lane == 0) {
+      sd_row_stats st;
+      st.argmax = a1;
+      st.top1 = t1;
+      st.top2 = t2;
+      st.pos = j;
+      st.lse = 0.0;
+      st.z_draft = part;
+      a.stats[m] = st;
+      s_arg[j] = a1;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool miss = lane < L && s_arg[lane] != a.draft_tokens[(size_t)r * gamma + lane];
+    const unsigned long long mask = __ballot(miss);
+    const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
+    if (lane == 0) {
+      accept_len[r] = acc;
+      next_token[r] = s_arg[acc];
+      if (counters) {
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)acc);
+      }
+    }
+  }
+}
+
 // Resident workgroups per CU of each persistent kernel, cached for the current device.
 struct Occupancy {
   int device = -1, cus = 0;
@@ -1022,6 +1125,16 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
     *n_part = (a.V + BN - 1) / BN;
     hipLaunchKernelGGL((k_gemm_tile<BM, BN>), dim3(n_mt * *n_part), dim3(256), 0, stream, a, n_mt, *n_part);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
+                                int64_t *counters, hipStream_t stream) {
+  int n_part = 0;
+  hipError_t e = launch_contraction(a, stream, &n_part);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_merge_accept_greedy, dim3(a.rm.B), dim3(64 * kFusedWaves), 0, stream, a,
+                     n_part, accept_len, next_token, counters);
   return hipGetLastError();
 }
 

@@ -119,6 +119,10 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
 
 // Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
+// Greedy verify in two launches: the contraction, then one kernel that merges each
+// request's row statistics and decides acceptance (temperature 0, stats written too).
+hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
+                                int64_t *counters, hipStream_t stream);
 // The contraction kernel alone; *n_part receives the partial columns written per row.
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part);
 

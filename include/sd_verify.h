@@ -155,6 +155,26 @@ SD_API int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_
                                      size_t workspace_bytes, void *stream);
 
 /*
+ * Greedy verify of a drafted block in one call (LFM2.5-DSpark blog, "How DSpark
+ * works" and "Quality parity"): the LM-head contraction at temperature 0 followed
+ * by one kernel that merges each request's row statistics and decides acceptance.
+ * Outputs are the same bytes as sd_verify_logits (temperature 0, logits NULL)
+ * followed by sd_accept_greedy, with one launch fewer.
+ *   hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma, d, V
+ *                as for sd_verify_logits (draft_tokens required)
+ *   stats        sd_row_stats [B * (gamma + 1)]  out, as for sd_verify_logits
+ *   accept_len, next_token, counters  as for sd_accept_greedy
+ *   workspace    the verify workspace (sd_verify_workspace_bytes)
+ * Errors: as for sd_verify_logits and sd_accept_greedy.
+ */
+SD_API int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
+                                const int32_t *draft_tokens, const int32_t *verify_len,
+                                const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                                int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                                int32_t *next_token, int64_t *counters, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * Greedy acceptance (LFM2.5-DSpark blog, "Quality parity"): a_r = first j < L_r
  * with stats[row_offsets[r] + j].argmax != draft_tokens[r][j], else L_r; the
  * emitted token is the target argmax of row a_r (a correction when a_r < L_r,

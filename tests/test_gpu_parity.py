@@ -68,6 +68,8 @@ SHAPES = [
     ("skinny32-rej", 1, 16, 264, 3000, 0.7, False),
     ("skinny64-trunc", 3, 16, 128, 777, 1.3, True),
     ("tiled-greedy", 9, 9, 512, 2050, 0.0, False),
+    ("tiled-d96-trunc", 20, 8, 96, 3000, 0.9, True),
+    ("tiled-d32-one-stage", 8, 16, 32, 777, 1.0, False),
     ("tiled-trunc-rej", 40, 16, 200, 5000, 1.0, True),
     ("gamma64", 2, 64, 64, 300, 1.0, False),
     ("many-requests", 300, 3, 64, 129, 0.0, True),
@@ -166,6 +168,37 @@ def test_determinism_bytes():
                                          vr.next_token, vr.row_offsets)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", [
+    ("greedy-block9", {}),
+    ("fused-trunc-skinny", dict(B=3, gamma=16, d=256, V=3001, truncate=True)),
+    ("fused-tiled", dict(B=20, gamma=8, d=128, V=5000, truncate=True)),
+    ("fused-gamma64", dict(B=2, gamma=64, d=64, V=700)),
+    ("fused-many", dict(B=300, gamma=3, d=64, V=129, truncate=True)),
+], ids=lambda c: c[0])
+def test_fused_greedy_matches_separate_calls(case):
+    """sd_verify_greedy writes the same bytes as sd_verify_logits + sd_accept_greedy."""
+    name, over = case
+    base = "greedy-block9" if name == "greedy-block9" else "ragged-b32"
+    over = dict(over, T=0.0, name=name) if name != "greedy-block9" else dict(name=name)
+    w = workload(base, **over)
+    W = make_weights(w)
+    W_dev = bf16_dev(W)
+    for step in range(2):
+        ds = upload_step(make_step(w, W, step))
+        outs = []
+        for fused in (True, False):
+            vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, 0.0, w.truncate, w.threshold, fused=fused)
+            vr.counters.zero_()
+            vr.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf)
+            torch.cuda.synchronize()
+            M = int(vr.row_offsets[-1].item()) if w.truncate else w.B * (w.gamma + 1)
+            outs.append([t.clone() for t in (vr.stats[:M], vr.accept_len, vr.next_token,
+                                             vr.counters)])
+            assert sd.device_flags(vr.ws_verify) == 0
+        for a, b in zip(*outs):
+            assert torch.equal(a, b)
 
 
 def test_rejection_lossless_on_gpu():
