@@ -1108,11 +1108,7 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
   if (cap <= 64) return launch_stream<4, 64, 128>(a, stream, n_part);
   constexpr int BM = 256;
   const int n_mt = (cap + BM - 1) / BM;
-  if (a.d % 64 == 0 && cap <= 1024) {        // a few hundred rows
-    constexpr int BN = 128;
-    *n_part = (a.V + BN - 1) / BN;
-    hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 3, 8>), dim3(n_mt * *n_part), dim3(512), 0, stream, a, n_mt, *n_part);
-  } else if (a.d % 64 == 0) {                 // many rows: bound by the matrix cores
+  if (a.d % 64 == 0) {
     constexpr int BN = 256;
     *n_part = (a.V + BN - 1) / BN;
     hipLaunchKernelGGL((k_gemm_dma<BM, BN, 64, 2, 8>), dim3(n_mt * *n_part), dim3(512), 0, stream, a, n_mt, *n_part);
