@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly, no HIP graph")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only the LM-head contraction kernel (for profiler runs)")
+    ap.add_argument("--accept-rate", action="store_true",
+                    help="rejection workloads: also compute the analytic acceptance rate of "
+                         "every verified position (sd_accept_rejection_ex)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB "
                          "(the known-size reference for the profiler's HBM byte counters)")
@@ -64,8 +67,9 @@ def contraction_kernel(w) -> str:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the contraction kernels are compiled from."""
     h = hashlib.sha256()
-    for f in ["sd_gemm.hip", "sd_accept.hip", "sd_internal.h"]:
+    for f in ["sd_gemm.hip", "sd_internal.h"]:
         with open(os.path.join(ROOT, "draft_block_verification_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -108,7 +112,8 @@ def main():
             draft_logits=None if s.draft_logits is None else bf16_dev(s.draft_logits),
             u_accept=torch.from_numpy(s.u_accept).to(dev),
             u_resample=torch.from_numpy(s.u_resample).to(dev)))
-    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev)
+    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev,
+                        accept_rate=args.accept_rate)
     stream = torch.cuda.Stream(device=dev)
 
     def step(i):
@@ -247,6 +252,7 @@ def main():
                    "temperature": w.T, "truncate": w.truncate, "distinct_steps": S,
                    "lm_head_copies": n_copies, "mean_rows": mean_rows,
                    "launch": "eager" if args.eager else "hipgraph",
+                   "accept_rate": vr.accept_rate is not None,
                    "timed": "verify only" if args.kernel_only else "truncate+verify+accept"},
         "roofline": roof,
         "cpu_baseline": cpu,

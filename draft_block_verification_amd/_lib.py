@@ -42,6 +42,8 @@ _SIGS = {
     "sd_accept_greedy": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sd_accept_rejection": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sd_accept_rejection_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                      _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -276,6 +278,34 @@ def sd_accept_rejection(logits: torch.Tensor, stats: torch.Tensor, draft_logits:
                         next_token: Optional[torch.Tensor] = None,
                         counters: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None):
+    accept_len, next_token, _ = _accept_rejection(
+        "sd_accept_rejection", logits, stats, draft_logits, draft_tokens, verify_len, row_offsets,
+        u_accept, u_resample, temperature, accept_len, next_token, counters, None, workspace,
+        stream)
+    return accept_len, next_token
+
+
+def sd_accept_rejection_ex(logits: torch.Tensor, stats: torch.Tensor, draft_logits: torch.Tensor,
+                           draft_tokens: torch.Tensor, verify_len: Optional[torch.Tensor],
+                           row_offsets: Optional[torch.Tensor], u_accept: torch.Tensor,
+                           u_resample: torch.Tensor, temperature: float,
+                           accept_len: Optional[torch.Tensor] = None,
+                           next_token: Optional[torch.Tensor] = None,
+                           counters: Optional[torch.Tensor] = None,
+                           accept_rate: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """sd_accept_rejection plus accept_rate float64 [B][gamma] (allocated when None)."""
+    B, g = draft_tokens.shape
+    if accept_rate is None:
+        accept_rate = torch.empty((B, g), dtype=torch.float64, device=draft_tokens.device)
+    return _accept_rejection("sd_accept_rejection_ex", logits, stats, draft_logits, draft_tokens,
+                             verify_len, row_offsets, u_accept, u_resample, temperature,
+                             accept_len, next_token, counters, accept_rate, workspace, stream)
+
+
+def _accept_rejection(name, logits, stats, draft_logits, draft_tokens, verify_len, row_offsets,
+                      u_accept, u_resample, temperature, accept_len, next_token, counters,
+                      accept_rate, workspace, stream):
     _need(draft_tokens, "draft_tokens", torch.int32)
     B, g = draft_tokens.shape
     dev = draft_tokens.device
@@ -292,13 +322,15 @@ def sd_accept_rejection(logits: torch.Tensor, stats: torch.Tensor, draft_logits:
         _need(counters, "counters", torch.int64, (2,))
     if workspace is None:
         workspace = new_workspace(accept_workspace_bytes(B, g, V), dev, stream)
-    _check("sd_accept_rejection",
-           _lib.sd_accept_rejection(_ptr(logits), _ptr(stats), _ptr(draft_logits),
-                                    _ptr(draft_tokens), _ptr(verify_len), _ptr(row_offsets),
-                                    _ptr(u_accept), _ptr(u_resample), B, g, V, float(temperature),
-                                    _ptr(accept_len), _ptr(next_token), _ptr(counters),
-                                    _ptr(workspace), workspace.numel(), _stream(stream)))
-    return accept_len, next_token
+    args = [_ptr(logits), _ptr(stats), _ptr(draft_logits), _ptr(draft_tokens), _ptr(verify_len),
+            _ptr(row_offsets), _ptr(u_accept), _ptr(u_resample), B, g, V, float(temperature),
+            _ptr(accept_len), _ptr(next_token), _ptr(counters)]
+    if name == "sd_accept_rejection_ex":
+        _need(accept_rate, "accept_rate", torch.float64, (B, g))
+        args.append(_ptr(accept_rate))
+    args += [_ptr(workspace), workspace.numel(), _stream(stream)]
+    _check(name, getattr(_lib, name)(*args))
+    return accept_len, next_token, accept_rate
 
 
 # --------------------------------------------------------------- a whole round
@@ -314,7 +346,7 @@ class VerifyRound:
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
                  truncate: bool, threshold: float = 0.3, device="cuda", stream=None,
-                 fused: bool = True):
+                 fused: bool = True, accept_rate: bool = False):
         self.B, self.gamma, self.d, self.V = B, gamma, d, V
         self.fused = fused
         self.T, self.truncate, self.threshold = float(temperature), truncate, float(threshold)
@@ -331,6 +363,9 @@ class VerifyRound:
         self.ws_verify = new_workspace(verify_workspace_bytes(B, gamma, d, V), dev, stream)
         self.ws_accept = (new_workspace(accept_workspace_bytes(B, gamma, V), dev, stream)
                           if self.T > 0 else None)
+        # Analytic acceptance rate per verified draft position (rejection rounds only).
+        self.accept_rate = (torch.empty((B, gamma), dtype=torch.float64, device=dev)
+                            if accept_rate and self.T > 0 else None)
 
     def run(self, hidden, lm_head, draft_tokens, conf=None, draft_logits=None, u_accept=None,
             u_resample=None, stream=None):
@@ -344,7 +379,12 @@ class VerifyRound:
             return self.accept_len, self.next_token
         sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                          self.T, self.logits, self.stats, self.ws_verify, stream=stream)
-        if self.T > 0:
+        if self.T > 0 and self.accept_rate is not None:
+            sd_accept_rejection_ex(self.logits, self.stats, draft_logits, draft_tokens,
+                                   self.verify_len, self.row_offsets, u_accept, u_resample,
+                                   self.T, self.accept_len, self.next_token, self.counters,
+                                   self.accept_rate, self.ws_accept, stream=stream)
+        elif self.T > 0:
             sd_accept_rejection(self.logits, self.stats, draft_logits, draft_tokens,
                                 self.verify_len, self.row_offsets, u_accept, u_resample, self.T,
                                 self.accept_len, self.next_token, self.counters, self.ws_accept,

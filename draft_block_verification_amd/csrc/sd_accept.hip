@@ -100,7 +100,9 @@ __global__ __launch_bounds__(256) void k_accept_greedy(const sd_row_stats *__res
 }
 
 // ----------------------------------------------------------- rejection accept
-// Four wide kernels, each over chunks of kChunk vocabulary ids:
+// Four wide kernels, each over chunks of kChunk vocabulary ids (grid x = chunk,
+// grid y strides over rows or requests, so that concurrent workgroups stream
+// neighbouring chunks of one row):
 //   k_draft_partial   (chunk, draft row): max and sum of exp((l - max) / T) of the
 //                     drafter logits, for every kept draft row;
 //   k_accept_decide   (request): merge those into log q-normalisers, then accept
@@ -136,6 +138,8 @@ struct RejArgs {
   int32_t *acc_a;            // [B] accepted length, -1 for a request outside the row capacity
   DraftPart *dpart;          // [B][gamma][C]
   double *csum;              // [B][C][2]: residual (or bonus) weight sum, p weight sum
+  double *rate_part;         // [B][gamma][C] acceptance-rate chunk sums, or null
+  double *rate;              // [B][gamma] acceptance rate out, or null
   WsHeader *ws;
 };
 
@@ -184,26 +188,28 @@ __device__ inline void load_draft_chunk(const uint16_t *row, int V, int c, float
 __global__ __launch_bounds__(256) void k_draft_partial(RejArgs a) {
   __shared__ float redf[4];
   __shared__ double redd[4];
-  const int gamma = a.rm.gamma;
-  const int r = blockIdx.y / gamma, j = blockIdx.y - r * gamma, c = blockIdx.x;
-  const int L = clamp_len(a.verify_len, r, gamma, threadIdx.x == 0 ? a.ws : nullptr);
-  if (j >= L) return;
-  const uint16_t *row = a.draft_logits + ((size_t)r * gamma + j) * a.V;
-  float x[kPer];
-  load_draft_chunk(row, a.V, c, x);
-  float cm = x[0];
+  const int gamma = a.rm.gamma, c = blockIdx.x;
+  for (int rj = blockIdx.y; rj < a.rm.B * gamma; rj += gridDim.y) {
+    const int r = rj / gamma, j = rj - r * gamma;
+    const int L = clamp_len(a.verify_len, r, gamma, threadIdx.x == 0 ? a.ws : nullptr);
+    if (j >= L) continue;
+    const uint16_t *row = a.draft_logits + (size_t)rj * a.V;
+    float x[kPer];
+    load_draft_chunk(row, a.V, c, x);
+    float cm = x[0];
 #pragma unroll
-  for (int e = 1; e < kPer; ++e) cm = fmaxf(cm, x[e]);
-  const float M = block_max_f(cm, redf);
-  float s = 0.f;
+    for (int e = 1; e < kPer; ++e) cm = fmaxf(cm, x[e]);
+    const float M = block_max_f(cm, redf);
+    float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (x[e] != -INFINITY) s += exp2f((x[e] - M) * a.sl);
-  const double S = block_sum_d((double)s, redd);
-  if (threadIdx.x == 0) {
-    DraftPart p;
-    p.m = M; p.pad = 0.f; p.s = S;
-    a.dpart[((size_t)r * gamma + j) * a.C + c] = p;
+    for (int e = 0; e < kPer; ++e)
+      if (x[e] != -INFINITY) s += exp2f((x[e] - M) * a.sl);
+    const double S = block_sum_d((double)s, redd);
+    if (threadIdx.x == 0) {
+      DraftPart p;
+      p.m = M; p.pad = 0.f; p.s = S;
+      a.dpart[(size_t)rj * a.C + c] = p;
+    }
   }
 }
 
@@ -322,11 +328,79 @@ __device__ inline void draw_weights(const DrawRow &d, int v, float *p, float *re
   }
 }
 
+// ------------------------------------------------------ analytic acceptance rate
+// c*_j = sum_v min(p_j(v), q_j(v)) = 1 - TV(p_j, q_j): the probability that the
+// rejection rule keeps position j when x_j is drawn from q_j (DSpark summary,
+// "Architecture": the confidence head's training label). The chunk sums ride along
+// in k_draw_partial's grid and k_draw_finalize adds them up in chunk order, so the
+// value does not depend on scheduling.
+__device__ void rate_chunk(const RejArgs &a, int rj, int c, double *red) {
+  const int gamma = a.rm.gamma;
+  const int r = rj / gamma, j = rj - r * gamma;
+  const int L = clamp_len(a.verify_len, r, gamma, nullptr);
+  if (j >= L) return;
+  const int base = request_base(a.rm, r, L, nullptr);
+  if (base < 0) return;
+  const float *z = a.logits + (size_t)(base + j) * a.V;
+  const uint16_t *q = a.draft_logits + (size_t)rj * a.V;
+  const double lse_p = a.stats[base + j].lse, lse_q = a.lse_q[rj];
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPer / 4; ++e) {
+    const int v0 = c * kChunk + 4 * (threadIdx.x + 256 * e);
+    float zf[4], ql[4];
+    if ((a.V & 3) == 0 && v0 + 4 <= a.V) {
+      const f32x4 zv = *reinterpret_cast<const f32x4 *>(z + v0);
+      const uint2 qv = *reinterpret_cast<const uint2 *>(q + v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zf[i] = zv[i];
+      ql[0] = __uint_as_float(qv.x << 16); ql[1] = __uint_as_float(qv.x & 0xffff0000u);
+      ql[2] = __uint_as_float(qv.y << 16); ql[3] = __uint_as_float(qv.y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = v0 + i < a.V;
+        zf[i] = in ? z[v0 + i] : 0.f;
+        ql[i] = in ? bf16_to_f32(q[v0 + i]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (v0 + i < a.V) {
+        const float p = expf((float)((double)zf[i] * a.invT - lse_p));
+        const float qq = expf((float)((double)ql[i] * a.invT - lse_q));
+        s += (double)fminf(p, qq);
+      }
+    }
+  }
+  s = block_sum_d(s, red);
+  if (threadIdx.x == 0) a.rate_part[(size_t)rj * a.C + c] = s;
+}
+
+// Request r's rates: wave w sums rows w, w + 4, ...; lane l takes chunks l, l + 64, ...
+// and a fixed butterfly adds the lanes. -1 marks positions that were not verified.
+__device__ void rate_finalize(const RejArgs &a, int r) {
+  const int gamma = a.rm.gamma, lane = threadIdx.x & 63;
+  const int L = clamp_len(a.verify_len, r, gamma, nullptr);
+  const bool ok = request_base(a.rm, r, L, nullptr) >= 0;
+  for (int j = threadIdx.x >> 6; j < gamma; j += 4) {
+    const size_t rj = (size_t)r * gamma + j;
+    if (j < L && ok) {
+      double s = 0.0;
+      for (int c = lane; c < a.C; c += 64) s += a.rate_part[rj * a.C + c];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) a.rate[rj] = s;
+    } else if (lane == 0) {
+      a.rate[rj] = -1.0;
+    }
+  }
+}
+
 // Chunk sums of the draw weights: ids c*kChunk + 4*(tid + 256 e) + i (16-byte logit
-// loads, each wave load 1 KB contiguous).
-__global__ __launch_bounds__(256) void k_draw_partial(RejArgs a) {
-  __shared__ double red[4];
-  const int r = blockIdx.y, c = blockIdx.x;
+// loads, each wave load 1 KB contiguous). Rows past B of k_draw_partial's row range
+// compute acceptance-rate chunk sums of draft row (row - B).
+__device__ void draw_chunk(const RejArgs &a, int r, int c, double *red) {
   DrawRow d;
   int arow;
   if (!draw_row(a, r, &d, &arow)) return;
@@ -371,10 +445,20 @@ __global__ __launch_bounds__(256) void k_draw_partial(RejArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_draw_partial(RejArgs a, int rows) {
+  __shared__ double red[4];
+  const int c = blockIdx.x;
+  for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+    if (r < a.rm.B) draw_chunk(a, r, c, red);
+    else rate_chunk(a, r - a.rm.B, c, red);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   __shared__ double s_d[8];
   __shared__ int s_i[12];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.rate) rate_finalize(a, r);
   DrawRow d;
   int arow;
   if (!draw_row(a, r, &d, &arow)) return;
@@ -521,6 +605,9 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   }
 }
 
+// Second grid dimension for a row range (the hardware bounds it at 65535).
+inline unsigned grid_rows(int rows) { return (unsigned)(rows < 65535 ? rows : 65535); }
+
 }  // namespace
 
 hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
@@ -557,7 +644,8 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
-                                   int64_t *counters, void *workspace, hipStream_t stream) {
+                                   int64_t *counters, double *accept_rate, void *workspace,
+                                   hipStream_t stream) {
   AcceptLayout l;
   accept_workspace_layout(rm.B, rm.gamma, V, &l);
   char *w = reinterpret_cast<char *>(workspace);
@@ -581,13 +669,19 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
   a.acc_a = reinterpret_cast<int32_t *>(w + l.acc_a);
   a.dpart = reinterpret_cast<DraftPart *>(w + l.dpart);
   a.csum = reinterpret_cast<double *>(w + l.csum);
+  // The drafter chunk partials are dead after k_accept_decide; their storage
+  // ([B][gamma][C] entries of 16 bytes) holds the rate chunk sums.
+  a.rate_part = accept_rate ? reinterpret_cast<double *>(w + l.dpart) : nullptr;
+  a.rate = accept_rate;
   a.ws = reinterpret_cast<WsHeader *>(workspace);
-  hipLaunchKernelGGL(k_draft_partial, dim3(l.chunks, rm.B * rm.gamma), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_draft_partial, dim3(l.chunks, grid_rows(rm.B * rm.gamma)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_draw_partial, dim3(l.chunks, rm.B), dim3(256), 0, stream, a);
+  const int draw_rows = rm.B + (accept_rate ? rm.B * rm.gamma : 0);
+  hipLaunchKernelGGL(k_draw_partial, dim3(l.chunks, grid_rows(draw_rows)), dim3(256), 0, stream, a,
+                     draw_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_draw_finalize, dim3(rm.B), dim3(256), 0, stream, a);
   return hipGetLastError();

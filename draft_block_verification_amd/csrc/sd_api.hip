@@ -218,6 +218,19 @@ int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
                             int32_t gamma, int32_t V, float temperature, int32_t *accept_len,
                             int32_t *next_token, int64_t *counters, void *workspace,
                             size_t workspace_bytes, void *stream) {
+  return sd_accept_rejection_ex(logits, stats, draft_logits, draft_tokens, verify_len,
+                                row_offsets, u_accept, u_resample, B, gamma, V, temperature,
+                                accept_len, next_token, counters, nullptr, workspace,
+                                workspace_bytes, stream);
+}
+
+int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
+                               const uint16_t *draft_logits, const int32_t *draft_tokens,
+                               const int32_t *verify_len, const int32_t *row_offsets,
+                               const float *u_accept, const float *u_resample, int32_t B,
+                               int32_t gamma, int32_t V, float temperature, int32_t *accept_len,
+                               int32_t *next_token, int64_t *counters, double *accept_rate,
+                               void *workspace, size_t workspace_bytes, void *stream) {
   if (!logits || !stats || !draft_logits || !draft_tokens || !u_accept || !u_resample ||
       !accept_len || !next_token)
     return SD_EINVAL;
@@ -227,6 +240,7 @@ int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
   if (!aligned(logits, 16) || !aligned(stats, 8) || !aligned(draft_logits, 16) ||
       !aligned(draft_tokens, 4) || !aligned(u_accept, 4) || !aligned(u_resample, 4) ||
       !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (accept_rate && !aligned(accept_rate, 8)) ||
       (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
     return SD_EALIGN;
   if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
@@ -235,7 +249,7 @@ int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stats,
   return launch_status(launch_accept_rejection(logits, stats, draft_logits, draft_tokens,
                                                verify_len, rm, u_accept, u_resample, V,
                                                temperature, accept_len, next_token, counters,
-                                               workspace, (hipStream_t)stream));
+                                               accept_rate, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -149,6 +149,7 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
-                                   int64_t *counters, void *workspace, hipStream_t stream);
+                                   int64_t *counters, double *accept_rate, void *workspace,
+                                   hipStream_t stream);
 
 }  // namespace sdv

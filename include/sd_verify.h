@@ -220,6 +220,28 @@ SD_API int32_t sd_accept_rejection(const float *logits, const sd_row_stats *stat
                             int32_t *next_token, int64_t *counters, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * sd_accept_rejection plus the analytic acceptance rate of every verified draft
+ * position (DSpark summary, "Architecture": the confidence head learns, per drafted
+ * position, the chance that rejection sampling keeps it, one minus the total-variation
+ * distance between drafter and target distributions):
+ *   accept_rate[r][j] = sum_v min(p_j(v), q_j(v)) = 1 - (1/2) sum_v |p_j(v) - q_j(v)|
+ * for j < L_r, with p_j, q_j as above at the same temperature; -1 for j >= L_r and for
+ * every position of a request whose rows leave the row capacity.
+ *   accept_rate  fp64 [B][gamma], 8-byte aligned, or NULL (then identical to
+ *                sd_accept_rejection)
+ * All other arguments, outputs and errors are those of sd_accept_rejection; the
+ * acceptance outputs are byte-identical to it. The extra work is one more pass over
+ * the kept target and drafter rows (P * V * 6 bytes), with the same workspace.
+ */
+SD_API int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
+                            const uint16_t *draft_logits, const int32_t *draft_tokens,
+                            const int32_t *verify_len, const int32_t *row_offsets,
+                            const float *u_accept, const float *u_resample, int32_t B,
+                            int32_t gamma, int32_t V, float temperature, int32_t *accept_len,
+                            int32_t *next_token, int64_t *counters, double *accept_rate,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -273,6 +273,31 @@ def accept_rejection(z: np.ndarray, draft_logit_bits: np.ndarray, draft_tokens: 
                                                            cdf_dist, residual, mass)
 
 
+def acceptance_rate(z: np.ndarray, draft_logit_bits: np.ndarray, verify_len: np.ndarray,
+                    row_offsets: np.ndarray, T: float, lse_p: Optional[np.ndarray] = None):
+    """Analytic per-position acceptance rate c*_j = 1 - TV(q_j, p_j).
+
+    DSpark summary, "Architecture" (confidence-scheduled verification): the confidence
+    head is trained on the acceptance probability of each drafted position, which for
+    the rejection rule is one minus the total-variation distance between the drafter's
+    and the target's distributions at that position, 1 - (1/2) * sum_v |q(v) - p(v)|.
+    Returns float64 [B][gamma]; positions at or past L_r hold -1 (not a probability).
+    """
+    assert T > 0
+    B, g = draft_logit_bits.shape[:2]
+    if lse_p is None:
+        lse_p = log_softmax_norm(np.asarray(z) / T)
+    out = np.full((B, g), -1.0)
+    for r in range(B):
+        base, L = int(row_offsets[r]), int(verify_len[r])
+        for j in range(L):
+            lq = bf16_decode(draft_logit_bits[r, j]) / T
+            q = np.exp(lq - log_softmax_norm(lq[None, :])[0])
+            p = np.exp(z[base + j] / T - lse_p[base + j])
+            out[r, j] = 1.0 - 0.5 * float(np.sum(np.abs(q - p)))
+    return out
+
+
 # ------------------------------------------------------------ whole round
 
 @dataclasses.dataclass

@@ -239,6 +239,56 @@ def test_rejection_lossless_on_gpu():
     assert abs(rate - want) < 4 * np.sqrt(want * (1 - want) / B)
 
 
+RATE_CASES = [
+    # (name, B, gamma, d, V, T, truncate, steps): chunk tails (V % 4096 != 0, V % 4 != 0),
+    # ragged rows, gamma = 64, and the full-size single-request rejection shape.
+    ("rate-small", 2, 5, 64, 1001, 1.0, False, 2),
+    ("rate-ragged", 12, 16, 128, 9000, 0.8, True, 2),
+    ("rate-gamma64", 2, 64, 64, 4099, 1.3, False, 1),
+    ("rate-rejection-b1", None, None, None, None, None, None, 2),
+]
+
+
+@pytest.mark.parametrize("case", RATE_CASES, ids=[c[0] for c in RATE_CASES])
+def test_acceptance_rate_matches_oracle(case):
+    """sd_accept_rejection_ex: 1 - TV(p_j, q_j) per verified position, abs 1e-4 against
+    the oracle; -1 past L_r; acceptance outputs byte-identical to sd_accept_rejection."""
+    name, B, g, d, V, T, trunc, steps = case
+    if B is None:
+        w = workload("rejection-b1")
+    else:
+        w = workload("ragged-b32", B=B, gamma=g, d=d, V=V, T=T, truncate=trunc,
+                     geo_p=(0.2,), name=name)
+    W = make_weights(w)
+    W64 = O.lm_head_f64(W)
+    W_dev = bf16_dev(W)
+    vr_ex = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold,
+                           accept_rate=True)
+    vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold)
+    worst = 0.0
+    for st in range(steps):
+        say(name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={st}")
+        s = make_step(w, W, st)
+        ds = upload_step(s)
+        g_ex = run_gpu(w, W_dev, ds, vr_ex)
+        g_pl = run_gpu(w, W_dev, ds, vr)
+        assert g_ex.flags == 0
+        assert np.array_equal(g_ex.accept_len, g_pl.accept_len)
+        assert np.array_equal(g_ex.next_token, g_pl.next_token)
+        assert np.array_equal(g_ex.counters, g_pl.counters)
+        rate_g = vr_ex.accept_rate.cpu().numpy()
+        o = run_oracle(w, W64, s)
+        rate_o = O.acceptance_rate(o.z, s.draft_logits, o.verify_len, o.row_offsets, w.T,
+                                   o.stats.lse)
+        live = rate_o >= 0
+        assert np.array_equal(rate_g < 0, ~live)
+        assert np.all(rate_g[~live] == -1.0)
+        err = float(np.max(np.abs(rate_g[live] - rate_o[live]))) if live.any() else 0.0
+        worst = max(worst, err)
+        assert err < 1e-4, f"acceptance rate error {err}"
+    say("report", f"max |rate err| {worst:.3g}")
+
+
 def test_out_of_range_lengths_are_clamped_and_flagged():
     w = workload("ragged-b32", B=4, V=2048, d=128, truncate=False, T=0.0, name="clamp")
     W = make_weights(w)

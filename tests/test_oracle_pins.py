@@ -256,6 +256,65 @@ def test_acceptance_rate_is_one_minus_tv():
     assert abs(acc_rate - (1 - 0.5 * np.abs(p - q).sum())) < 2.0 / N
 
 
+def test_acceptance_rate_function_matches_integrated_acceptance():
+    """acceptance_rate against the rejection rule itself, integrated exactly over u and x.
+
+    For x ~ q the rule keeps x with probability min(1, p(x)/q(x)); summing q(x) times
+    that over every x is the acceptance rate. The ratios come from accept_rejection's
+    diagnostics, a separate route through the oracle.
+    """
+    rng = np.random.default_rng(31)
+    V, g, T = 7, 3, 0.8
+    zt = bf16_to_f32(bf16_round(rng.standard_normal((g + 1, V)).astype(np.float32)))
+    dl = bf16_round(rng.standard_normal((1, g, V)).astype(np.float32) * 1.5)
+    z = zt.astype(np.float64)
+    vlen, offs = np.array([g], np.int32), np.array([0, g + 1], np.int32)
+    rate = O.acceptance_rate(z, dl, vlen, offs, T)
+    assert rate.shape == (1, g)
+    q = _softmax_rows(bf16_to_f32(dl[0]).astype(np.float64) / T)
+    integ = np.zeros(g)
+    for x in range(V):
+        res, diag = O.accept_rejection(z, dl, np.full((1, g), x, np.int32), vlen, offs,
+                                       np.zeros((1, g), np.float32),
+                                       np.zeros((1, g + 1), np.float32), T)
+        integ += q[:, x] * np.minimum(1.0, diag.ratio[0, :g])
+    assert np.allclose(rate[0], integ, rtol=0, atol=1e-12)
+
+
+def test_acceptance_rate_closed_forms_and_ragged_rows():
+    """V = 2: rate = 1 - |p(0) - q(0)|; p = q gives 1, disjoint supports give 0, and
+    positions past L_r hold -1. Rows are packed with per-request offsets, so a shifted
+    row or request index changes a value."""
+    T = 1.0
+    vlen = np.array([3, 0, 2], np.int32)
+    offs = np.concatenate([[0], np.cumsum(vlen + 1)]).astype(np.int32)
+    g = 3
+    rng = np.random.default_rng(5)
+    a = rng.uniform(0.05, 0.95, offs[-1])
+    z = np.stack([np.log(a), np.log1p(-a)], axis=1)
+    ld = rng.standard_normal((3, g, 2)).astype(np.float32)
+    dl = bf16_round(ld)
+    # Request 2 position 0: the drafter equals the target row (bf16-exact logits).
+    dl[2, 0] = bf16_round(np.array([0.5, -0.25], np.float32))
+    z[offs[2]] = [0.5, -0.25]
+    # Request 2 position 1: disjoint supports.
+    dl[2, 1] = bf16_round(np.array([-300.0, 0.0], np.float32))
+    z[offs[2] + 1] = [0.0, -900.0]
+    rate = O.acceptance_rate(z, dl, vlen, offs, T)
+    for r in range(3):
+        for j in range(g):
+            if j >= vlen[r]:
+                assert rate[r, j] == -1.0
+                continue
+            zr = z[offs[r] + j]
+            p0 = 1.0 / (1.0 + np.exp(zr[1] - zr[0]))
+            lq = bf16_to_f32(dl[r, j]).astype(np.float64)
+            q0 = 1.0 / (1.0 + np.exp(lq[1] - lq[0]))
+            assert abs(rate[r, j] - (1.0 - abs(p0 - q0))) < 1e-12
+    assert abs(rate[2, 0] - 1.0) < 1e-15
+    assert abs(rate[2, 1]) < 1e-100
+
+
 def test_rejection_is_lossless_chi2():
     """DSpark summary, "Problem definition": rejection sampling keeps the target distribution.
 
