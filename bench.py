@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--accept-rate", action="store_true",
                     help="rejection workloads: also compute the analytic acceptance rate of "
                          "every verified position (sd_accept_rejection_ex)")
+    ap.add_argument("--scheduler", choices=["threshold", "early-stop", "top-k"],
+                    default="threshold",
+                    help="truncating workloads: confidence threshold (default) or the "
+                         "hardware-aware prefix scheduler on an SPS table profiled at start "
+                         "(top-k sizes the batch from the confidences of two steps before)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB "
                          "(the known-size reference for the profiler's HBM byte counters)")
@@ -103,23 +108,42 @@ def main():
     n_copies = max(1, math.ceil(2 * MALL_BYTES / w_bytes)) if w_bytes < MALL_BYTES else 1
     W_dev = [bf16_dev(W) for _ in range(n_copies)]
     steps_host = [make_step(w, W, i) for i in range(S)]
+    def conditional(conf):
+        """Per-position conditional confidences c_k = s_k / s_(k-1) of survival curves s."""
+        c = conf.astype(np.float32).copy()
+        c[:, 1:] = conf[:, 1:] / conf[:, :-1]
+        return c
+
     staged = []
     for s in steps_host:
         staged.append(dict(
             hidden=bf16_dev(s.hidden),
             draft_tokens=torch.from_numpy(s.draft_tokens).to(dev),
             conf=None if s.conf is None else torch.from_numpy(s.conf).to(dev),
+            cond=None if s.conf is None else torch.from_numpy(conditional(s.conf)).to(dev),
             draft_logits=None if s.draft_logits is None else bf16_dev(s.draft_logits),
             u_accept=torch.from_numpy(s.u_accept).to(dev),
             u_resample=torch.from_numpy(s.u_resample).to(dev)))
+    sched = None
+    sps = None
+    if args.scheduler != "threshold":
+        if not w.truncate:
+            sys.exit(f"--scheduler needs a truncating workload; {w.name} verifies whole blocks")
+        sched = sd.SCHED_EARLY_STOP if args.scheduler == "early-stop" else sd.SCHED_TOP_K
+        sps = sd.profile_sps(w.B, w.gamma, W_dev[0], w.T)
     vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev,
-                        accept_rate=args.accept_rate)
+                        accept_rate=args.accept_rate, scheduler=sched, sps=sps)
     stream = torch.cuda.Stream(device=dev)
+
+    # The threshold reads survival confidences; the scheduler reads the conditional ones
+    # (its own running product rebuilds the survival).
+    conf_key = "conf" if sched is None else "cond"
 
     def step(i):
         st = staged[i % S]
-        vr.run(st["hidden"], W_dev[i % n_copies], st["draft_tokens"], st["conf"],
-               st["draft_logits"], st["u_accept"], st["u_resample"])
+        stale = staged[(i - 2) % S]["cond"] if sched == sd.SCHED_TOP_K else None
+        vr.run(st["hidden"], W_dev[i % n_copies], st["draft_tokens"], st[conf_key],
+               st["draft_logits"], st["u_accept"], st["u_resample"], conf_stale=stale)
 
     def verify_only(i):
         # The contraction kernel alone: the same launch sd_verify_logits starts with.
@@ -171,16 +195,26 @@ def main():
         ms_total = timed(step, K, Wu)
         positions = int(vr.counters[0].item())
     # Rows per step from the same staged inputs (a truncation pass per distinct step).
-    rows = []
-    for i in range(S):
-        st = staged[i]
-        if w.truncate:
+    def rows_of(i):
+        """(rows, expected tokens) of step i: tau = R + sum of the admitted survivals."""
+        st = staged[i % S]
+        if not w.truncate:
+            return w.B * (w.gamma + 1), None
+        if sched is None:
             vl, _ = sd.sd_truncate_by_confidence(st["conf"], w.threshold)
-            rows.append(int(vl.sum().item()) + w.B)
         else:
-            rows.append(w.B * (w.gamma + 1))
+            stale = staged[(i - 2) % S]["cond"] if sched == sd.SCHED_TOP_K else None
+            vl, _ = sd.sd_schedule_prefix(st["cond"], sps, sched, stale)
+        vl = vl.cpu().numpy()
+        surv = steps_host[i % S].conf
+        tau = w.B + float(sum(surv[r, :vl[r]].astype(np.float64).sum() for r in range(w.B)))
+        return int(vl.sum()) + w.B, tau
+
+    by_phase = [rows_of(i) for i in range(S)]      # rows depend on the step only through i % S
+    mean_rows = float(np.mean([by_phase[i % S][0] for i in range(Wu, Wu + K)]))
+    tau = (float(np.mean([by_phase[i % S][1] for i in range(Wu, Wu + K)])) if w.truncate
+           else None)
     torch.cuda.synchronize()
-    mean_rows = float(np.mean([rows[i % S] for i in range(Wu, Wu + K)]))
     if positions is None:
         positions = int(round((mean_rows - w.B) * K))
 
@@ -253,6 +287,10 @@ def main():
                    "lm_head_copies": n_copies, "mean_rows": mean_rows,
                    "launch": "eager" if args.eager else "hipgraph",
                    "accept_rate": vr.accept_rate is not None,
+                   "scheduler": args.scheduler,
+                   # Expected tokens per second if the confidences are calibrated survival
+                   # probabilities: (R + admitted survivals) per step / step time.
+                   "expected_tokens_per_s": None if tau is None else tau / (ms_step * 1e-3),
                    "timed": "verify only" if args.kernel_only else "truncate+verify+accept"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 import torch
@@ -33,6 +33,7 @@ _SIGS = {
     "sd_workspace_init": (_i32, [_vp, _sz, _vp]),
     "sd_device_flags": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32), _i32]),
     "sd_truncate_by_confidence": (_i32, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "sd_schedule_prefix": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
     "sd_verify_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                 _vp, _sz, _vp]),
     "sd_verify_contraction": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
@@ -146,6 +147,89 @@ def sd_truncate_by_confidence(conf: torch.Tensor, threshold: float,
            _lib.sd_truncate_by_confidence(_ptr(conf), B, g, float(threshold), _ptr(verify_len),
                                           _ptr(row_offsets), _stream(stream)))
     return verify_len, row_offsets
+
+
+SCHED_EARLY_STOP, SCHED_TOP_K = 0, 1
+SCHED_MAX_CANDIDATES = 16384
+
+
+def sd_schedule_prefix(conf: torch.Tensor, sps: torch.Tensor, mode: int = SCHED_EARLY_STOP,
+                       conf_stale: Optional[torch.Tensor] = None,
+                       verify_len: Optional[torch.Tensor] = None,
+                       row_offsets: Optional[torch.Tensor] = None, stream=None):
+    """Hardware-aware prefix scheduler; same outputs as sd_truncate_by_confidence."""
+    _need(conf, "conf", torch.float32)
+    R, g = conf.shape
+    _need(sps, "sps", torch.float32)
+    if conf_stale is not None:
+        _need(conf_stale, "conf_stale", torch.float32, (R, g))
+    if verify_len is None:
+        verify_len = torch.empty(R, dtype=torch.int32, device=conf.device)
+    if row_offsets is None:
+        row_offsets = torch.empty(R + 1, dtype=torch.int32, device=conf.device)
+    _need(verify_len, "verify_len", torch.int32, (R,))
+    _need(row_offsets, "row_offsets", torch.int32, (R + 1,))
+    _check("sd_schedule_prefix",
+           _lib.sd_schedule_prefix(_ptr(conf), _ptr(conf_stale), R, g, _ptr(sps), sps.numel(),
+                                   int(mode), _ptr(verify_len), _ptr(row_offsets),
+                                   _stream(stream)))
+    return verify_len, row_offsets
+
+
+def profile_sps(R: int, gamma: int, lm_head: torch.Tensor, temperature: float = 0.0,
+                breakpoints: Optional[Sequence[int]] = None, repeats: int = 10,
+                stream=None) -> torch.Tensor:
+    """Steps-per-second table SPS(B), B = 0 .. R * (gamma + 1), of this library's own verify
+    call (sd_verify_logits) for R requests with gamma drafts each.
+
+    The verify cost is a staircase in the number of rows B (the contraction works on
+    row tiles), so it is timed at the top of each stair -- every multiple of 256 rows
+    and the full capacity, by default -- and every B takes the rate of the first timed
+    point at or above it. Returns fp32 [R * (gamma + 1) + 1] on lm_head's device.
+    """
+    _need(lm_head, "lm_head", torch.bfloat16)
+    V, d = lm_head.shape
+    dev = lm_head.device
+    cap = R * (gamma + 1)
+    if breakpoints is None:
+        breakpoints = sorted({min(cap, max(R, 256 * i)) for i in range(1, cap // 256 + 1)} | {cap})
+    breakpoints = sorted({int(b) for b in breakpoints if R <= int(b) <= cap} | {cap})
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    hidden = (torch.randn((R, gamma + 1, d), generator=gen) / 4).to(torch.bfloat16).to(dev)
+    drafts = torch.randint(0, V, (R, gamma), generator=gen, dtype=torch.int32).to(dev)
+    stats = new_stats(R, gamma, dev)
+    logits = (torch.empty((cap, V), dtype=torch.float32, device=dev) if temperature > 0
+              else None)
+    ws = new_workspace(verify_workspace_bytes(R, gamma, d, V), dev, stream)
+    st = torch.cuda.Stream(device=dev) if stream is None else stream
+    times = []
+    for rows in breakpoints:
+        extra = rows - R
+        L = [min(gamma, max(0, extra - gamma * r)) for r in range(R)]
+        offs = [0]
+        for x in L:
+            offs.append(offs[-1] + x + 1)
+        vl = torch.tensor(L, dtype=torch.int32, device=dev)
+        ro = torch.tensor(offs, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(st):
+            for _ in range(2):
+                sd_verify_logits(hidden, lm_head, drafts, vl, ro, temperature, logits, stats, ws,
+                                 stream=st)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(repeats):
+                sd_verify_logits(hidden, lm_head, drafts, vl, ro, temperature, logits, stats, ws,
+                                 stream=st)
+            e1.record(st)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / repeats)
+    sps = torch.empty(cap + 1, dtype=torch.float32)
+    i = 0
+    for B in range(cap + 1):
+        while breakpoints[i] < B:
+            i += 1
+        sps[B] = 1e3 / times[i]
+    return sps.to(dev)
 
 
 def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
@@ -346,8 +430,14 @@ class VerifyRound:
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
                  truncate: bool, threshold: float = 0.3, device="cuda", stream=None,
-                 fused: bool = True, accept_rate: bool = False):
+                 fused: bool = True, accept_rate: bool = False, scheduler: Optional[int] = None,
+                 sps: Optional[torch.Tensor] = None):
         self.B, self.gamma, self.d, self.V = B, gamma, d, V
+        # With a scheduler mode (SCHED_EARLY_STOP / SCHED_TOP_K) and an SPS table, the
+        # prefix scheduler replaces the confidence threshold.
+        self.scheduler, self.sps = scheduler, sps
+        if scheduler is not None and (not truncate or sps is None):
+            raise ValueError("a scheduler needs truncate=True and an SPS table")
         self.fused = fused
         self.T, self.truncate, self.threshold = float(temperature), truncate, float(threshold)
         dev = torch.device(device)
@@ -368,8 +458,12 @@ class VerifyRound:
                             if accept_rate and self.T > 0 else None)
 
     def run(self, hidden, lm_head, draft_tokens, conf=None, draft_logits=None, u_accept=None,
-            u_resample=None, stream=None):
-        if self.truncate:
+            u_resample=None, stream=None, conf_stale=None):
+        if self.truncate and self.scheduler is not None:
+            sd_schedule_prefix(conf, self.sps, self.scheduler,
+                               conf_stale if self.scheduler == SCHED_TOP_K else None,
+                               self.verify_len, self.row_offsets, stream=stream)
+        elif self.truncate:
             sd_truncate_by_confidence(conf, self.threshold, self.verify_len, self.row_offsets,
                                       stream=stream)
         if self.T == 0 and self.fused:

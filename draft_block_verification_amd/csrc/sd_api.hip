@@ -107,6 +107,23 @@ int32_t sd_truncate_by_confidence(const float *conf, int32_t B, int32_t gamma, f
                                        (hipStream_t)stream));
 }
 
+int32_t sd_schedule_prefix(const float *conf, const float *conf_stale, int32_t R, int32_t gamma,
+                           const float *sps, int32_t n_sps, int32_t mode, int32_t *verify_len,
+                           int32_t *row_offsets, void *stream) {
+  static_assert(kSchedMaxCandidates == SD_SCHED_MAX_CANDIDATES, "candidate bound");
+  if (!conf || !sps || !verify_len || !row_offsets) return SD_EINVAL;
+  if (mode != SD_SCHED_EARLY_STOP && mode != SD_SCHED_TOP_K) return SD_EINVAL;
+  if (mode == SD_SCHED_EARLY_STOP && conf_stale) return SD_EINVAL;
+  if (R < 1 || gamma < 1 || gamma > kMaxGamma) return SD_ESHAPE;
+  if ((int64_t)R * gamma > kSchedMaxCandidates) return SD_ESHAPE;
+  if ((int64_t)n_sps < (int64_t)R * (gamma + 1) + 1) return SD_ESHAPE;
+  if (!aligned(conf, 4) || !aligned(sps, 4) || !aligned(verify_len, 4) ||
+      !aligned(row_offsets, 4) || (conf_stale && !aligned(conf_stale, 4)))
+    return SD_EALIGN;
+  return launch_status(launch_schedule(conf, conf_stale, R, gamma, sps, mode, verify_len,
+                                       row_offsets, (hipStream_t)stream));
+}
+
 namespace {
 
 // Shared validation and argument set-up of sd_verify_logits / sd_verify_contraction.

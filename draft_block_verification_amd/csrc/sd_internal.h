@@ -129,6 +129,12 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
 hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
                            int32_t *verify_len, int32_t *row_offsets, hipStream_t stream);
 
+// Prefix scheduler: one workgroup sorts all R * gamma candidates in LDS.
+constexpr int kSchedMaxCandidates = 16384;
+hipError_t launch_schedule(const float *conf, const float *conf_stale, int R, int gamma,
+                           const float *sps, int mode, int32_t *verify_len, int32_t *row_offsets,
+                           hipStream_t stream);
+
 hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,
                                 const int32_t *verify_len, const RowMap &rm,
                                 int32_t *accept_len, int32_t *next_token, int64_t *counters,

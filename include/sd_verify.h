@@ -3,6 +3,7 @@
  *
  * One verify round of speculative decoding on an AMD MI355X (gfx950):
  *   1. sd_truncate_by_confidence  keep each request's confident draft prefix
+ *      sd_schedule_prefix         or choose the prefixes that maximise throughput
  *   2. sd_verify_logits           LM-head logits at every kept position plus the
  *                                 bonus position, with per-row statistics
  *   3. sd_accept_greedy           greedy prefix acceptance + correction/bonus token
@@ -117,6 +118,48 @@ SD_API int32_t sd_device_flags(void *workspace, void *stream, uint32_t *flags, i
  *   row_offsets int32 [B + 1]    out: exclusive prefix sum of (L_r + 1); row_offsets[B] = M
  */
 SD_API int32_t sd_truncate_by_confidence(const float *conf, int32_t B, int32_t gamma, float threshold,
+                                  int32_t *verify_len, int32_t *row_offsets, void *stream);
+
+/* Modes of sd_schedule_prefix. */
+enum {
+    SD_SCHED_EARLY_STOP = 0,  /* synchronous: admit by survival, stop when throughput drops */
+    SD_SCHED_TOP_K = 1        /* asynchronous: K from (stale) confidences over every K, then top-K */
+};
+
+/* Largest R * gamma sd_schedule_prefix accepts (all candidates are sorted in one workgroup). */
+#define SD_SCHED_MAX_CANDIDATES 16384
+
+/*
+ * Hardware-aware prefix scheduler (DSpark summary, "Architecture" ->
+ * "Confidence-Scheduled Verification": survival-ordered admission that maximises
+ * throughput tau * SPS(B) over a cost table profiled once, with early stopping;
+ * "Engineering": the asynchronous form that sizes the batch from two-step-old
+ * confidences by a search over every K and admits the current top-K). A drop-in
+ * replacement for sd_truncate_by_confidence.
+ *   conf        fp32 [R][gamma]  conditional confidences c[r][k] of the current step
+ *   conf_stale  fp32 [R][gamma]  confidences of an earlier step (SD_SCHED_TOP_K only,
+ *               may be NULL: then conf); must be NULL with SD_SCHED_EARLY_STOP
+ *   sps         fp32 [n_sps]     steps per second at a batch of B target rows, for
+ *               B = 0 .. n_sps - 1; n_sps >= R * (gamma + 1) + 1; finite and positive
+ *   mode        SD_SCHED_EARLY_STOP or SD_SCHED_TOP_K
+ *   verify_len  int32 [R]        out: admitted drafts of request r (a prefix of its block)
+ *   row_offsets int32 [R + 1]    out: exclusive prefix sum of (verify_len + 1)
+ * Survival a[r][j] = product of clamp(c[r][k], 0, 1) over k <= j (NaN counts as 0),
+ * taken left to right in fp32. Candidates are ordered by larger survival, then lower
+ * request, then lower position. With K admitted, the batch is B = R + K rows and
+ * Theta_K = (R * 2^40 + sum over the first K candidates of floor(a * 2^40)) * SPS(B),
+ * the integer converted to fp64 (round to nearest even) and one fp64 multiply.
+ * SD_SCHED_EARLY_STOP: K = first K with Theta_{K+1} < Theta_K, else R * gamma.
+ * SD_SCHED_TOP_K: K = smallest K attaining the largest Theta_K over K = 0 .. R * gamma
+ * (computed from conf_stale when given); the admitted set is the first K candidates
+ * in the order of conf.
+ * Errors: SD_EINVAL for a null output or conf/sps, a bad mode or a stale array with
+ * SD_SCHED_EARLY_STOP; SD_ESHAPE for R < 1, gamma outside [1, 64],
+ * R * gamma > SD_SCHED_MAX_CANDIDATES or a short sps table; SD_EALIGN for arrays not
+ * 4-byte aligned. One workgroup, no workspace.
+ */
+SD_API int32_t sd_schedule_prefix(const float *conf, const float *conf_stale, int32_t R,
+                                  int32_t gamma, const float *sps, int32_t n_sps, int32_t mode,
                                   int32_t *verify_len, int32_t *row_offsets, void *stream);
 
 /*

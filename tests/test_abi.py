@@ -103,3 +103,39 @@ def test_truncate_and_accept_host_validation():
     small_ws = list(args)
     small_ws[16] = ctypes.c_size_t(64)
     assert r(*small_ws) == 4
+
+
+def test_accept_rejection_ex_host_validation():
+    r = lib.sd_accept_rejection_ex
+    args = [FAKE] * 8 + [1, 4, 1024, ctypes.c_float(1.0)] + [FAKE, FAKE, None, FAKE, FAKE,
+                                                             ctypes.c_size_t(1 << 20), None]
+    bad_rate = list(args)
+    bad_rate[15] = ctypes.c_void_p(0x10004)           # fp64 output must be 8-byte aligned
+    assert r(*bad_rate) == 3
+    bad_T = list(args)
+    bad_T[11] = ctypes.c_float(0.0)
+    assert r(*bad_T) == 1
+    small_ws = list(args)
+    small_ws[17] = ctypes.c_size_t(64)
+    assert r(*small_ws) == 4
+
+
+def test_schedule_prefix_host_validation():
+    f = lib.sd_schedule_prefix
+
+    def call(conf=FAKE, stale=None, R=4, g=16, sps=FAKE, n=4 * 17 + 1, mode=0, vl=FAKE,
+             ro=FAKE):
+        return f(conf, stale, ctypes.c_int32(R), ctypes.c_int32(g), sps, ctypes.c_int32(n),
+                 ctypes.c_int32(mode), vl, ro, None)
+
+    assert call(conf=None) == 1
+    assert call(sps=None) == 1
+    assert call(vl=None) == 1
+    assert call(mode=2) == 1
+    assert call(stale=FAKE, mode=0) == 1              # stale confidences only with top-K
+    assert call(R=0) == 2
+    assert call(g=65) == 2
+    assert call(n=4 * 17) == 2                        # table must reach B = R * (gamma + 1)
+    assert call(R=1025, g=16, n=1025 * 17 + 1) == 2  # more than 16384 candidates
+    assert call(conf=MISALIGNED) == 3
+    assert call(stale=MISALIGNED, mode=1) == 3
