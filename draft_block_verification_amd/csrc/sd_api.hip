@@ -28,7 +28,7 @@ int32_t check_sizes(int32_t B, int32_t gamma, int32_t d, int32_t V) {
 }
 
 size_t verify_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
-  return verify_workspace_layout(B, gamma, V, nullptr, nullptr);
+  return verify_workspace_layout(B, gamma, V, nullptr, nullptr, nullptr);
 }
 
 size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
@@ -143,9 +143,9 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head,
     return SD_EALIGN;
   if (!workspace || workspace_bytes < verify_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
-  size_t part_off = 0;
+  size_t part_off = 0, zx_off = 0;
   int part_stride = 0;
-  verify_workspace_layout(B, gamma, V, &part_off, &part_stride);
+  verify_workspace_layout(B, gamma, V, &part_off, &part_stride, &zx_off);
   char *wsb = reinterpret_cast<char *>(workspace);
   VerifyArgs &a = *out;
   a.hidden = hidden;
@@ -161,6 +161,7 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head,
   a.logits = logits;
   a.partials = reinterpret_cast<TilePartial *>(wsb + part_off);
   a.part_stride = part_stride;
+  a.zx = reinterpret_cast<double *>(wsb + zx_off);
   a.stats = stats;
   a.ws = reinterpret_cast<WsHeader *>(workspace);
   return SD_OK;
@@ -192,7 +193,8 @@ int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
                                   workspace_bytes, &a);
   if (st != SD_OK) return st;
   int n_part = 0;
-  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part));
+  bool zx_done = false;
+  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part, &zx_done));
 }
 
 int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,

@@ -331,6 +331,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     }
   }
 
+  // Drafted token of packed row `lane` (M <= 16 MT <= 64), when the drafted-token
+  // logits are produced here: LM-head row x passes through LDS while its slab streams,
+  // so the workgroup owning that slab forms the exact fp64 dot of the bf16 hidden and
+  // LM-head rows from the staged data. Wave w takes the w-th such row of a slab;
+  // rows past the fourth of one slab are marked NaN and left to the merge.
+  int zslab = -1, ztok = 0;
+  if (a.zx && a.draft_tokens && lane < M) {
+    int rq, jj;
+    if (hidden_row(a.rm, lane, &rq, &jj) >= 0 && jj < clamp_len(a.verify_len, rq, a.rm.gamma, nullptr)) {
+      const int x = a.draft_tokens[(size_t)rq * a.rm.gamma + jj];
+      if (x >= 0 && x < V) { zslab = x / BN; ztok = x; }
+    }
+  }
+  unsigned long long zmask = 0ull;
+  int zrow = -1, zw = 0;
+  double zacc = 0.0;
+
   const int nslab = (V + BN - 1) / BN;
   const int nst = d / KC;
   const int total = ((nslab - g + G - 1) / G) * nst;   // (slab, stage) pairs of this workgroup
@@ -386,6 +403,27 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[i], 0, 0, 0);
       }
     }
+    if (t % nst == 0) {
+      // First stage of a slab: which rows drafted a token of it.
+      const int slab = g + (t / nst) * G;
+      zmask = __ballot(zslab == slab);
+      unsigned long long mm = zmask;
+      for (int i = 0; i < wave && mm; ++i) mm &= mm - 1;
+      zrow = mm ? __ffsll((long long)mm) - 1 : -1;
+      zw = __shfl(ztok, zrow >= 0 ? zrow : 0) - slab * BN;
+      zacc = 0.0;
+    }
+    if (zrow >= 0 && lane < CH) {
+      // Lane l takes logical chunk l (8 values) of the staged hidden and LM-head rows.
+      const int hrow = BN + zrow;
+      const u32x4 hv = *(const LDSP u32x4 *)(Sb + hrow * KC + 8 * (lane ^ (hrow & 15)));
+      const u32x4 wv = *(const LDSP u32x4 *)(Sb + zw * KC + 8 * (lane ^ (zw & 15)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zacc += (double)__uint_as_float(hv[e] << 16) * (double)__uint_as_float(wv[e] << 16);
+        zacc += (double)__uint_as_float(hv[e] & 0xffff0000u) * (double)__uint_as_float(wv[e] & 0xffff0000u);
+      }
+    }
     if (t % nst == nst - 1) {
       // Slab done. Lane l holds rows 16 i + 4 (l >> 4) + q, vocabulary id v; reduce
       // over the 16 lanes that share l >> 4.
@@ -417,6 +455,17 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         }
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (zrow >= 0) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) zacc += __shfl_xor(zacc, off);
+        if (lane == 0) a.zx[zrow] = zacc;
+      }
+      if (tid == 0 && zmask) {
+        unsigned long long mm = zmask;
+        for (int i = 0; i < 4 && mm; ++i) mm &= mm - 1;
+        for (; mm; mm &= mm - 1) a.zx[__ffsll((long long)mm) - 1] = __longlong_as_double(0x7ff8000000000000ll);
+      }
+      zrow = -1;
     }
   }
 
@@ -813,10 +862,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
 }
 
 // One workgroup per verified row: merge the row's partials (loaded in one round of
-// independent loads, kMergePer per thread) and compute the drafted token's exact logit,
+// independent loads, kMergePer per thread) and write the drafted token's exact logit,
 // an fp64 dot of the bf16 hidden and LM-head rows (bf16 x bf16 products are exact in
-// fp64). The hidden row is loaded before the partials, the LM-head row as soon as the
-// drafted token id is known, so the three memory round trips overlap.
+// fp64). The skinny contraction leaves that logit in a.zx; otherwise (or where it
+// marked NaN) the rows are loaded right after the partials and dotted here.
 constexpr int kMergePer = 16;   // partials per thread per round (n <= 4096 in one round)
 constexpr int kDotPer = 4;      // 16-byte chunks per thread held for the dot (d <= 8192)
 
@@ -838,12 +887,9 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
       j < clamp_len(a.verify_len, r, a.rm.gamma, tid == 0 ? a.ws : nullptr))
     x = a.draft_tokens[(size_t)r * a.rm.gamma + j];
   const bool has_x = x >= 0 && x < a.V;        // uniform across the workgroup
-  u32x4 hv[kDotPer];
-#pragma unroll
-  for (int i = 0; i < kDotPer; ++i) {
-    const int c = tid + 256 * i;
-    hv[i] = has_x && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
+  // The drafted token's logit from the contraction, when it left one (NaN: not there).
+  double zg = 0.0;
+  if (has_x && a.zx) zg = a.zx[m];
 
   const TilePartial *P = a.partials + (size_t)m * a.part_stride;
   float t1 = -INFINITY, t2 = -INFINITY;
@@ -861,12 +907,20 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
       else { t2 = fmaxf(t2, q[i].top1); }
     }
   }
+  // Without a logit from the contraction, the hidden and LM-head rows for the dot.
+  const bool need_dot = has_x && (!a.zx || zg != zg);
+  u32x4 hv[kDotPer];
+#pragma unroll
+  for (int i = 0; i < kDotPer; ++i) {
+    const int c = tid + 256 * i;
+    hv[i] = need_dot && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
   const uint16_t *wrow = a.W + (size_t)(has_x ? x : 0) * a.d;
   u32x4 wv[kDotPer];
 #pragma unroll
   for (int i = 0; i < kDotPer; ++i) {
     const int c = tid + 256 * i;
-    wv[i] = has_x && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    wv[i] = need_dot && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
 
 #pragma unroll
@@ -899,8 +953,8 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
     S = block_sum(S, red);
     lse = (double)t1 * a.invT + log(S);
   }
-  double zd = 0.0;
-  if (has_x) {
+  double zd = has_x ? zg : 0.0;
+  if (need_dot) {
     double part = 0.0;
     auto dot8 = [&](const u32x4 &h, const u32x4 &w) {
 #pragma unroll
@@ -928,7 +982,7 @@ constexpr int kFusedPer = 8;    // loads in flight per lane
 __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
     VerifyArgs a, int n, int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
     int64_t *__restrict__ counters) {
-  __shared__ int s_arg[65];
+  __shared__ int s_arg[65], s_x[64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gamma = a.rm.gamma;
   const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
@@ -945,8 +999,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
   const int nc = a.d / 8;
   for (int j = wave; j <= L; j += kFusedWaves) {
     const int m = base + j;
+    // The drafted token, its logit from the contraction when that left one, and the
+    // partials are loaded together; only without a logit (NaN or none) are the hidden
+    // and LM-head rows read for the fp64 dot.
     const int x = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
     const bool has_x = x >= 0 && x < a.V;
+    double zg = 0.0;
+    if (has_x && a.zx) zg = a.zx[m];
     const TilePartial *P = a.partials + (size_t)m * a.part_stride;
     float t1 = -INFINITY, t2 = -INFINITY;
     int a1 = 0x7fffffff;
@@ -963,8 +1022,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
         else { t2 = fmaxf(t2, q[i].top1); }
       }
     }
+    const bool need_dot = has_x && (!a.zx || zg != zg);
     double part = 0.0;
-    if (has_x) {
+    if (need_dot) {
       const uint16_t *h = a.hidden + ((size_t)r * (gamma + 1) + j) * a.d;
       const uint16_t *w = a.W + (size_t)x * a.d;
       for (int c0 = 0; c0 < nc; c0 += 64 * kFusedPer) {
@@ -1000,14 +1060,15 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
       st.top2 = t2;
       st.pos = j;
       st.lse = 0.0;
-      st.z_draft = part;
+      st.z_draft = need_dot ? part : (has_x ? zg : 0.0);
       a.stats[m] = st;
       s_arg[j] = a1;
+      if (j < L) s_x[j] = x;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    const bool miss = lane < L && s_arg[lane] != a.draft_tokens[(size_t)r * gamma + lane];
+    const bool miss = lane < L && s_arg[lane] != s_x[lane];
     const unsigned long long mask = __ballot(miss);
     const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
     if (lane == 0) {
@@ -1087,17 +1148,23 @@ hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
 
 }  // namespace
 
-size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride) {
+size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride,
+                               size_t *zx_off) {
   const size_t cap = (size_t)B * (gamma + 1);
   const int stride = (V + kMinVocabTile - 1) / kMinVocabTile;
   const size_t po = sizeof(WsHeader);
+  const size_t zo = po + align_up(cap * (size_t)stride * sizeof(TilePartial), 256);
   if (part_off) *part_off = po;
   if (part_stride) *part_stride = stride;
-  return po + align_up(cap * (size_t)stride * sizeof(TilePartial), 256);
+  if (zx_off) *zx_off = zo;
+  return zo + align_up(cap * sizeof(double), 256);
 }
 
-hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
+                              bool *zx_done) {
   const int cap = a.rm.B * (a.rm.gamma + 1);
+  *zx_done = false;
+  if (a.d % 128 == 0 && cap <= 64) *zx_done = a.zx != nullptr && a.draft_tokens != nullptr;
   if (a.d % 128 == 0) {
     if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part);
     if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part);
@@ -1127,18 +1194,24 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
 hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
                                 int64_t *counters, hipStream_t stream) {
   int n_part = 0;
-  hipError_t e = launch_contraction(a, stream, &n_part);
+  bool zx_done = false;
+  hipError_t e = launch_contraction(a, stream, &n_part, &zx_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge_accept_greedy, dim3(a.rm.B), dim3(64 * kFusedWaves), 0, stream, a,
+  VerifyArgs m = a;
+  if (!zx_done) m.zx = nullptr;
+  hipLaunchKernelGGL(k_merge_accept_greedy, dim3(a.rm.B), dim3(64 * kFusedWaves), 0, stream, m,
                      n_part, accept_len, next_token, counters);
   return hipGetLastError();
 }
 
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
   int n_part = 0;
-  hipError_t e = launch_contraction(a, stream, &n_part);
+  bool zx_done = false;
+  hipError_t e = launch_contraction(a, stream, &n_part, &zx_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, a, n_part);
+  VerifyArgs m = a;
+  if (!zx_done) m.zx = nullptr;
+  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, m, n_part);
   return hipGetLastError();
 }
 

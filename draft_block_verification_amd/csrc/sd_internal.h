@@ -110,12 +110,15 @@ struct VerifyArgs {
   float *logits;                // fp32 [cap][V] or null
   TilePartial *partials;        // [cap][part_stride]
   int part_stride;
+  double *zx;                   // [cap] drafted-token logits left by the contraction (NaN:
+                                // not computed there), or null when it leaves none
   sd_row_stats *stats;          // [cap]
   WsHeader *ws;
 };
 
 // Bytes of verify workspace (header, then the row partials) for these sizes.
-size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride);
+size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride,
+                               size_t *zx_off);
 
 // Host-side launchers (defined in sd_gemm.hip / sd_accept.hip). Return hipError_t.
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
@@ -123,8 +126,10 @@ hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 // request's row statistics and decides acceptance (temperature 0, stats written too).
 hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
                                 int64_t *counters, hipStream_t stream);
-// The contraction kernel alone; *n_part receives the partial columns written per row.
-hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part);
+// The contraction kernel alone; *n_part receives the partial columns written per row and
+// *zx_done whether it also wrote the drafted-token logits to a.zx.
+hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
+                              bool *zx_done);
 
 hipError_t launch_truncate(const float *conf, int B, int gamma, float threshold,
                            int32_t *verify_len, int32_t *row_offsets, hipStream_t stream);

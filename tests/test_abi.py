@@ -44,7 +44,7 @@ def test_workspace_sizes():
     # Header, then one 16-byte partial per (row, 64-wide vocabulary tile).
     up = lambda x: (x + 255) // 256 * 256
     b = sd.verify_workspace_bytes(1, 9, 2048, 32768)
-    assert b == 256 + up(10 * 512 * 16)
+    assert b == 256 + up(10 * 512 * 16) + up(10 * 8)   # partials, then fp64 drafted-token logits
     assert sd.verify_workspace_bytes(32, 16, 4096, 151936) >= 32 * 17 * (151936 // 64) * 16
     assert sd.accept_workspace_bytes(128, 16, 129280) >= 256 + 128 * 16 * 8 + 128 * 16 * 32 * 16
     for bad in [(0, 9, 2048, 100), (1, 0, 2048, 100), (1, 65, 2048, 100), (1, 4, 12, 100),

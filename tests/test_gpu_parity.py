@@ -239,6 +239,40 @@ def test_rejection_lossless_on_gpu():
     assert abs(rate - want) < 4 * np.sqrt(want * (1 - want) / B)
 
 
+CROWDED = [
+    # (name, B, gamma, d, V, T): every drafted token in the first 64 vocabulary ids, so
+    # one LM-head slab holds up to 51 drafted rows (the skinny contraction forms the
+    # first four logits itself and leaves the rest to the merge).
+    ("crowded-greedy", 1, 16, 256, 3000, 0.0),
+    ("crowded-rej", 3, 16, 512, 3001, 1.0),
+    ("crowded-trunc", 2, 20, 384, 2000, 0.8),
+]
+
+
+@pytest.mark.parametrize("case", CROWDED, ids=[c[0] for c in CROWDED])
+def test_drafted_tokens_crowding_one_slab(case):
+    name, B, g, d, V, T = case
+    w = workload("ragged-b32", B=B, gamma=g, d=d, V=V, T=T, truncate=name.endswith("trunc"),
+                 geo_p=(0.2,), name=name)
+    W = make_weights(w)
+    W64 = O.lm_head_f64(W)
+    W_dev = bf16_dev(W)
+    rng = np.random.default_rng(7)
+    rep = Report()
+    for fused in (True, False):
+        vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, fused=fused)
+        for st in range(2):
+            say(name, f"B={B} g={g} d={d} V={V} T={T} step={st} fused={fused}")
+            s = make_step(w, W, st)
+            s.draft_tokens = rng.integers(0, 64, s.draft_tokens.shape).astype(np.int32)
+            g_res = run_gpu(w, W_dev, upload_step(s), vr, fetch_all_logits=w.T > 0)
+            o = attach_inputs(run_oracle(w, W64, s), s)
+            assert g_res.flags == 0
+            compare(w, g_res, o, range(w.B), rep)
+            assert np.array_equal(g_res.counters, o.accept.counters)
+    say("report", rep)
+
+
 RATE_CASES = [
     # (name, B, gamma, d, V, T, truncate, steps): chunk tails (V % 4096 != 0, V % 4 != 0),
     # ragged rows, gamma = 64, and the full-size single-request rejection shape.
