@@ -73,6 +73,9 @@ SHAPES = [
     ("tiled-trunc-rej", 40, 16, 200, 5000, 1.0, True),
     ("gamma64", 2, 64, 64, 300, 1.0, False),
     ("many-requests", 300, 3, 64, 129, 0.0, True),
+    # More vocabulary tiles than the chip holds at once (a second, partial round).
+    ("tiled-two-rounds-rej", 5, 16, 64, 70000, 1.0, True),
+    ("tiled-two-rounds-greedy", 4, 20, 128, 69999, 0.0, False),
 ]
 
 
