@@ -1,0 +1,81 @@
+"""Pins of the W12 oracle (oracle/w12.py) against things other than itself.
+
+Exact round trips over every one of the 65536 bf16 bit patterns and over
+synthetic LM heads; bytes of a hand-encoded group; the edges of the exponent
+window; the layout of the correction slots.
+"""
+import numpy as np
+
+from oracle import w12 as X
+from synth import make_weights, workload
+
+
+def test_round_trip_every_bf16_pattern():
+    """Zeros, subnormals, infinities, NaNs and every exponent come back bit for bit."""
+    W = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(512, 128)
+    rng = np.random.default_rng(0)
+    W = W[rng.permutation(512)]                      # mix the exponents across rows
+    enc = X.encode(W)
+    assert enc.base == 254 - 14                      # largest finite normal exponent is 254
+    assert np.array_equal(X.decode(enc, 512, 128), W)
+    assert enc.codes.shape == (512, 16, 12) and enc.codes.dtype == np.uint8
+
+
+def test_round_trip_synthetic_lm_head_and_few_corrections():
+    w = workload("tiny-greedy")
+    W = make_weights(w)                               # N(0, 1/sqrt(d)) in bf16, V=1024, d=256
+    enc = X.encode(W)
+    assert np.array_equal(X.decode(enc, *W.shape), W)
+    n_corr = int(np.count_nonzero(enc.corr))
+    assert n_corr < 1e-3 * W.size                    # the window holds almost every weight
+    assert enc.cap % 4 == 0 and enc.cap >= 4
+
+
+def test_hand_encoded_group_and_correction():
+    """One row of 128: the first group by hand, a tiny weight as a correction."""
+    row = np.zeros(128, dtype=np.uint16)
+    row[:8] = [0x3F80, 0xC000, 0x3F00, 0x0000, 0x8000, 0x4040, 0x3FC0, 0x3F40]
+    #          1.0     -2.0    0.5     +0      -0      3.0     1.5     0.75
+    row[9] = 0x3580                                   # 2^-20: exponent 107 < window start
+    enc = X.encode(row[None, :])
+    assert enc.base == 128 - 14                       # 3.0 and -2.0 have exponent 128
+    # codes: 1.0 -> 0x700, -2.0 -> 0xF80, 0.5 -> 0x680, +0 -> 0, -0 -> 0x800,
+    #        3.0 -> 0x7C0, 1.5 -> 0x740, 0.75 -> 0x6C0
+    assert enc.codes[0, 0].tolist() == [0x00, 0x80, 0x80, 0x00, 0x00, 0xC0, 0x40, 0xC0,
+                                        0xF7, 0x06, 0x78, 0x67]
+    assert enc.codes[0, 1, 1] == 0x00 and enc.codes[0, 1, 8] == 0x00   # placeholder +0
+    assert enc.cap == 4
+    assert enc.corr[0, 0].tolist() == [0x35800009, 0, 0, 0]
+    assert np.array_equal(X.decode(enc, 1, 128), row[None, :])
+
+
+def test_window_edges():
+    """E_max - 14 is the lowest coded exponent; E_max - 15 needs a correction."""
+    row = np.full(128, 0x3F80, dtype=np.uint16)       # 1.0, exponent 127
+    row[1] = (127 - 14) << 7                          # coded with c = 1
+    row[2] = (127 - 15) << 7                          # one below the window
+    row[3] = 0x0001                                   # subnormal
+    row[4] = 0x7F80                                   # +inf
+    enc = X.encode(row[None, :])
+    assert enc.base == 127 - 14
+    lo, hi = enc.codes[0, 0, 1], enc.codes[0, 0, 8] >> 4
+    assert (int(hi) << 8 | int(lo)) == 1 << 7
+    ks = sorted(int(e) & 0x7F for e in enc.corr[0, 0] if e)
+    assert ks == [2, 3, 4]
+    assert np.array_equal(X.decode(enc, 1, 128), row[None, :])
+
+
+def test_correction_regions_and_order():
+    """Regions are 64 rows by 128 columns; slots sorted by (row, column); CAP rounds up."""
+    V, d = 130, 256
+    W = np.full((V, d), 0x3F80, dtype=np.uint16)
+    tiny = 0x0400                                     # exponent 8: far below the window
+    spots = [(0, 5), (0, 3), (63, 127), (64, 0), (129, 200), (129, 130), (1, 3), (2, 0), (3, 1)]
+    for v, k in spots:
+        W[v, k] = tiny
+    enc = X.encode(W)
+    assert enc.corr.shape == (3, 2, 8)                # fullest region holds 6 -> CAP 8
+    first = [int(e) for e in enc.corr[0, 0] if e]
+    assert [((e >> 7) & 0x3F, e & 0x7F) for e in first] == [(0, 3), (0, 5), (1, 3), (2, 0), (3, 1), (63, 127)]
+    assert [int(e) & 0xFFFF for e in enc.corr[2, 1] if e] == [2 | 1 << 7, 72 | 1 << 7]
+    assert np.array_equal(X.decode(enc, V, d), W)
