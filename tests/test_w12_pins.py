@@ -16,7 +16,7 @@ def test_round_trip_every_bf16_pattern():
     rng = np.random.default_rng(0)
     W = W[rng.permutation(512)]                      # mix the exponents across rows
     enc = X.encode(W)
-    assert enc.base == 254 - 14                      # largest finite normal exponent is 254
+    assert enc.b2 == 127 - 6                          # inf / NaN patterns have e2 = 127
     assert np.array_equal(X.decode(enc, 512, 128), W)
     assert enc.codes.shape == (512, 16, 12) and enc.codes.dtype == np.uint8
 
@@ -27,7 +27,7 @@ def test_round_trip_synthetic_lm_head_and_few_corrections():
     enc = X.encode(W)
     assert np.array_equal(X.decode(enc, *W.shape), W)
     n_corr = int(np.count_nonzero(enc.corr))
-    assert n_corr < 1e-3 * W.size                    # the window holds almost every weight
+    assert n_corr < 5e-3 * W.size                    # the window holds almost every weight
     assert enc.cap % 4 == 0 and enc.cap >= 4
 
 
@@ -36,32 +36,32 @@ def test_hand_encoded_group_and_correction():
     row = np.zeros(128, dtype=np.uint16)
     row[:8] = [0x3F80, 0xC000, 0x3F00, 0x0000, 0x8000, 0x4040, 0x3FC0, 0x3F40]
     #          1.0     -2.0    0.5     +0      -0      3.0     1.5     0.75
-    row[9] = 0x3580                                   # 2^-20: exponent 107 < window start
+    row[9] = 0x3580                                   # 2^-20: e2 = 0x35, below the window
     enc = X.encode(row[None, :])
-    assert enc.base == 128 - 14                       # 3.0 and -2.0 have exponent 128
-    # codes: 1.0 -> 0x700, -2.0 -> 0xF80, 0.5 -> 0x680, +0 -> 0, -0 -> 0x800,
-    #        3.0 -> 0x7C0, 1.5 -> 0x740, 0.75 -> 0x6C0
-    assert enc.codes[0, 0].tolist() == [0x00, 0x80, 0x80, 0x00, 0x00, 0xC0, 0x40, 0xC0,
-                                        0xF7, 0x06, 0x78, 0x67]
-    assert enc.codes[0, 1, 1] == 0x00 and enc.codes[0, 1, 8] == 0x00   # placeholder +0
+    assert enc.b2 == 0x40 - 6                         # -2.0 and 3.0 have e2 = 0x40
+    # codes (sign << 3 | t): 1.0 -> 6, -2.0 -> 0xF, 0.5 -> 6, +0 -> 0, -0 -> 8,
+    # 3.0 -> 7, 1.5 -> 6, 0.75 -> 6; low bytes verbatim
+    assert enc.codes[0, 0].tolist() == [0x80, 0x00, 0x00, 0x00, 0x00, 0x40, 0xC0, 0x40,
+                                        0xF6, 0x06, 0x78, 0x66]
+    assert enc.codes[0, 1].tolist() == [0] * 12       # placeholder +0 for column 9
     assert enc.cap == 4
     assert enc.corr[0, 0].tolist() == [0x35800009, 0, 0, 0]
     assert np.array_equal(X.decode(enc, 1, 128), row[None, :])
 
 
 def test_window_edges():
-    """E_max - 14 is the lowest coded exponent; E_max - 15 needs a correction."""
-    row = np.full(128, 0x3F80, dtype=np.uint16)       # 1.0, exponent 127
-    row[1] = (127 - 14) << 7                          # coded with c = 1
-    row[2] = (127 - 15) << 7                          # one below the window
+    """e2_max - 6 is the lowest pair in the window; e2_max - 7 needs a correction;
+    zeros, subnormals and exponent 1 are coded (t = 0)."""
+    row = np.full(128, 0x3F80, dtype=np.uint16)       # 1.0: e2 = 63
+    row[1] = 57 << 8                                  # coded with t = 1
+    row[2] = 56 << 8                                  # one below the window
     row[3] = 0x0001                                   # subnormal
-    row[4] = 0x7F80                                   # +inf
+    row[4] = 0x8000                                   # -0
+    row[5] = 0x0080                                   # exponent 1
     enc = X.encode(row[None, :])
-    assert enc.base == 127 - 14
-    lo, hi = enc.codes[0, 0, 1], enc.codes[0, 0, 8] >> 4
-    assert (int(hi) << 8 | int(lo)) == 1 << 7
-    ks = sorted(int(e) & 0x7F for e in enc.corr[0, 0] if e)
-    assert ks == [2, 3, 4]
+    assert enc.b2 == 57
+    assert enc.codes[0, 0, 8] >> 4 == 1 and enc.codes[0, 0, 1] == 0x00
+    assert [int(e) & 0x7F for e in enc.corr[0, 0] if e] == [2]
     assert np.array_equal(X.decode(enc, 1, 128), row[None, :])
 
 
@@ -69,7 +69,7 @@ def test_correction_regions_and_order():
     """Regions are 64 rows by 128 columns; slots sorted by (row, column); CAP rounds up."""
     V, d = 130, 256
     W = np.full((V, d), 0x3F80, dtype=np.uint16)
-    tiny = 0x0400                                     # exponent 8: far below the window
+    tiny = 0x0400                                     # e2 = 4: far below the window
     spots = [(0, 5), (0, 3), (63, 127), (64, 0), (129, 200), (129, 130), (1, 3), (2, 0), (3, 1)]
     for v, k in spots:
         W[v, k] = tiny
