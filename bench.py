@@ -57,6 +57,9 @@ def parse():
                     help="truncating workloads: confidence threshold (default) or the "
                          "hardware-aware prefix scheduler on an SPS table profiled at start "
                          "(top-k sizes the batch from the confidences of two steps before)")
+    ap.add_argument("--weights", choices=["bf16", "w12"], default="bf16",
+                    help="LM-head format: bf16, or the lossless W12 stream (streaming regime "
+                         "only; encoded on the host before timing)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB "
                          "(the known-size reference for the profiler's HBM byte counters)")
@@ -104,9 +107,15 @@ def main():
 
     # ---- stage inputs in HBM
     W = make_weights(w)
-    w_bytes = W.nbytes
+    if args.weights == "w12":
+        enc = sd.w12_encode(W)
+        w_bytes = enc[0].nbytes + enc[1].nbytes
+        make_head = lambda: sd.W12Weights(*enc, device=dev)
+    else:
+        w_bytes = W.nbytes
+        make_head = lambda: bf16_dev(W)
     n_copies = max(1, math.ceil(2 * MALL_BYTES / w_bytes)) if w_bytes < MALL_BYTES else 1
-    W_dev = [bf16_dev(W) for _ in range(n_copies)]
+    W_dev = [make_head() for _ in range(n_copies)]
     steps_host = [make_step(w, W, i) for i in range(S)]
     def conditional(conf):
         """Per-position conditional confidences c_k = s_k / s_(k-1) of survival curves s."""
@@ -222,8 +231,8 @@ def main():
     # It runs on the row layout the last step left in place (truncation included).
     rows_c = int(vr.row_offsets[-1].item()) if w.truncate else w.B * (w.gamma + 1)
     ms_verify = timed(verify_only, K, Wu) / K
-    # Algorithmic bytes: the LM head once plus the verified hidden rows.
-    v_bytes = w.V * w.d * 2 + rows_c * w.d * 2
+    # Algorithmic bytes: the LM head once (in its stored format) plus the verified hidden rows.
+    v_bytes = w_bytes + rows_c * w.d * 2
     v_flops = 2.0 * rows_c * w.V * w.d
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if v_flops / v_bytes > ridge:
@@ -237,7 +246,7 @@ def main():
     tr_path = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
-        ent = tr.get(w.name)
+        ent = tr.get(w.name if args.weights == "bf16" else f"{w.name}-{args.weights}")
         if ent and ent.get("kernel_hash") == kernel_source_hash():
             roof["traffic"] = ent["bytes_per_launch"]
     roof["kernel"] = contraction_kernel(w)
@@ -288,6 +297,7 @@ def main():
                    "launch": "eager" if args.eager else "hipgraph",
                    "accept_rate": vr.accept_rate is not None,
                    "scheduler": args.scheduler,
+                   "lm_head_format": args.weights,
                    # Expected tokens per second if the confidences are calibrated survival
                    # probabilities: (R + admitted survivals) per step / step time.
                    "expected_tokens_per_s": None if tau is None else tau / (ms_step * 1e-3),

@@ -34,6 +34,13 @@ _SIGS = {
     "sd_device_flags": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32), _i32]),
     "sd_truncate_by_confidence": (_i32, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
     "sd_schedule_prefix": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "sd_w12_encode": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "sd_verify_logits_w12": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                    _vp, _sz, _vp]),
+    "sd_verify_contraction_w12": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                         _sz, _vp]),
+    "sd_verify_greedy_w12": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                    _vp, _vp, _sz, _vp]),
     "sd_verify_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                 _vp, _sz, _vp]),
     "sd_verify_contraction": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
@@ -232,20 +239,86 @@ def profile_sps(R: int, gamma: int, lm_head: torch.Tensor, temperature: float = 
     return sps.to(dev)
 
 
+class _SdW12(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("corr", ctypes.c_void_p), ("cap", ctypes.c_int32),
+                ("b2", ctypes.c_int32)]
+
+
+def w12_encode(W_bits: np.ndarray):
+    """Host W12 encoding of a bf16 LM head (uint16 bit patterns [V][d]) by the library's
+    sd_w12_encode: returns (codes uint8 [V/64][d/128][64][16][12] (region-blocked),
+    corr uint32 [V/64][d/128][cap], cap, b2, V)."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    V, d = W_bits.shape
+    cap, b2 = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("sd_w12_encode", _lib.sd_w12_encode(W_bits.ctypes.data, V, d, None, None,
+                                               ctypes.byref(cap), ctypes.byref(b2)))
+    codes = np.empty(((V + 63) // 64, d // 128, 64, 16, 12), dtype=np.uint8)
+    corr = np.empty(((V + 63) // 64, d // 128, cap.value), dtype=np.uint32)
+    _check("sd_w12_encode", _lib.sd_w12_encode(W_bits.ctypes.data, V, d, codes.ctypes.data,
+                                               corr.ctypes.data, ctypes.byref(cap),
+                                               ctypes.byref(b2)))
+    return codes, corr, int(cap.value), int(b2.value), V
+
+
+class W12Weights:
+    """A W12 LM head in device memory: 12-byte groups, correction slots, window start.
+    Pass it as `lm_head` to sd_verify_logits / sd_verify_greedy / VerifyRound."""
+
+    def __init__(self, codes: np.ndarray, corr: np.ndarray, cap: int, b2: int, V: int,
+                 device="cuda"):
+        self.V, self.d = int(V), codes.shape[1] * 128
+        self.cap, self.b2 = int(cap), int(b2)
+        self.codes = torch.from_numpy(np.ascontiguousarray(codes)).to(device)
+        self.corr = torch.from_numpy(np.ascontiguousarray(corr).view(np.int32)).to(device)
+        self.shape = (self.V, self.d)
+        self.nbytes = self.codes.numel() + 4 * self.corr.numel()
+        self._desc = _SdW12(self.codes.data_ptr(), self.corr.data_ptr(), self.cap, self.b2)
+
+    @classmethod
+    def from_bf16(cls, W_bits: np.ndarray, device="cuda") -> "W12Weights":
+        return cls(*w12_encode(W_bits), device=device)
+
+    def descriptor(self):
+        return ctypes.byref(self._desc)
+
+
+def sd_verify_logits_w12(hidden, lm_head: W12Weights, *args, **kwargs):
+    return sd_verify_logits(hidden, lm_head, *args, **kwargs)
+
+
+def sd_verify_contraction_w12(hidden, lm_head: W12Weights, *args, **kwargs):
+    return sd_verify_contraction(hidden, lm_head, *args, **kwargs)
+
+
+def sd_verify_greedy_w12(hidden, lm_head: W12Weights, *args, **kwargs):
+    return sd_verify_greedy(hidden, lm_head, *args, **kwargs)
+
+
+def _lm_head(lm_head, d):
+    """(pointer or descriptor, V, is_w12) of a bf16 LM head tensor or W12Weights."""
+    if isinstance(lm_head, W12Weights):
+        if lm_head.d != d:
+            raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+        return lm_head.descriptor(), lm_head.V, True
+    _need(lm_head, "lm_head", torch.bfloat16)
+    if lm_head.shape[1] != d:
+        raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+    return _ptr(lm_head), lm_head.shape[0], False
+
+
 def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
                      draft_tokens: Optional[torch.Tensor] = None,
                      verify_len: Optional[torch.Tensor] = None,
                      row_offsets: Optional[torch.Tensor] = None, temperature: float = 0.0,
                      logits: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
-    """Returns (logits or None, stats). Pass logits=True to have one allocated."""
+    """Returns (logits or None, stats). Pass logits=True to have one allocated.
+    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_logits_w12 runs)."""
     _need(hidden, "hidden", torch.bfloat16)
-    _need(lm_head, "lm_head", torch.bfloat16)
     B, g1, d = hidden.shape
     g = g1 - 1
-    V = lm_head.shape[0]
-    if lm_head.shape[1] != d:
-        raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+    head, V, w12 = _lm_head(lm_head, d)
     dev = hidden.device
     if draft_tokens is not None:
         _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
@@ -262,10 +335,11 @@ def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
     _need(stats, "stats", torch.int64, (B * g1, 4))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
-    _check("sd_verify_logits",
-           _lib.sd_verify_logits(_ptr(hidden), _ptr(lm_head), _ptr(draft_tokens), _ptr(verify_len),
-                                 _ptr(row_offsets), B, g, d, V, float(temperature), _ptr(logits),
-                                 _ptr(stats), _ptr(workspace), workspace.numel(), _stream(stream)))
+    name = "sd_verify_logits_w12" if w12 else "sd_verify_logits"
+    _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(draft_tokens), _ptr(verify_len),
+                                     _ptr(row_offsets), B, g, d, V, float(temperature),
+                                     _ptr(logits), _ptr(stats), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
     return logits, stats
 
 
@@ -274,20 +348,19 @@ def sd_verify_contraction(hidden: torch.Tensor, lm_head: torch.Tensor,
                           row_offsets: Optional[torch.Tensor] = None, temperature: float = 0.0,
                           logits: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None):
-    """The contraction stage alone (logits and workspace partials, no row statistics)."""
+    """The contraction stage alone (logits and workspace partials, no row statistics).
+    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_contraction_w12 runs)."""
     _need(hidden, "hidden", torch.bfloat16)
-    _need(lm_head, "lm_head", torch.bfloat16)
     B, g1, d = hidden.shape
-    V = lm_head.shape[0]
+    head, V, w12 = _lm_head(lm_head, d)
     if logits is not None:
         _need(logits, "logits", torch.float32, (B * g1, V))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g1 - 1, d, V), hidden.device, stream)
-    _check("sd_verify_contraction",
-           _lib.sd_verify_contraction(_ptr(hidden), _ptr(lm_head), _ptr(verify_len),
-                                      _ptr(row_offsets), B, g1 - 1, d, V, float(temperature),
-                                      _ptr(logits), _ptr(workspace), workspace.numel(),
-                                      _stream(stream)))
+    name = "sd_verify_contraction_w12" if w12 else "sd_verify_contraction"
+    _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(verify_len), _ptr(row_offsets), B,
+                                     g1 - 1, d, V, float(temperature), _ptr(logits),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)))
     return logits
 
 
@@ -299,14 +372,12 @@ def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: 
                      next_token: Optional[torch.Tensor] = None,
                      counters: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
-    """Greedy verify in one call: returns (stats, accept_len, next_token)."""
+    """Greedy verify in one call: returns (stats, accept_len, next_token).
+    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_greedy_w12 runs)."""
     _need(hidden, "hidden", torch.bfloat16)
-    _need(lm_head, "lm_head", torch.bfloat16)
     B, g1, d = hidden.shape
     g = g1 - 1
-    V = lm_head.shape[0]
-    if lm_head.shape[1] != d:
-        raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+    head, V, w12 = _lm_head(lm_head, d)
     dev = hidden.device
     _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
     if verify_len is not None:
@@ -323,11 +394,11 @@ def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: 
         _need(counters, "counters", torch.int64, (2,))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
-    _check("sd_verify_greedy",
-           _lib.sd_verify_greedy(_ptr(hidden), _ptr(lm_head), _ptr(draft_tokens), _ptr(verify_len),
-                                 _ptr(row_offsets), B, g, d, V, _ptr(stats), _ptr(accept_len),
-                                 _ptr(next_token), _ptr(counters), _ptr(workspace),
-                                 workspace.numel(), _stream(stream)))
+    name = "sd_verify_greedy_w12" if w12 else "sd_verify_greedy"
+    _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(draft_tokens), _ptr(verify_len),
+                                     _ptr(row_offsets), B, g, d, V, _ptr(stats), _ptr(accept_len),
+                                     _ptr(next_token), _ptr(counters), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
     return stats, accept_len, next_token
 
 

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdverify.so")
-SOURCES = ["sd_api.hip", "sd_gemm.hip", "sd_accept.hip", "sd_sched.hip"]
+SOURCES = ["sd_api.hip", "sd_gemm.hip", "sd_accept.hip", "sd_sched.hip", "sd_w12.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

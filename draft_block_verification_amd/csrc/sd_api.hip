@@ -127,17 +127,26 @@ int32_t sd_schedule_prefix(const float *conf, const float *conf_stale, int32_t R
 namespace {
 
 // Shared validation and argument set-up of sd_verify_logits / sd_verify_contraction.
-int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head,
+int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
                      const int32_t *draft_tokens, const int32_t *verify_len,
                      const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d, int32_t V,
                      float temperature, float *logits, sd_row_stats *stats, bool need_stats,
                      void *workspace, size_t workspace_bytes, VerifyArgs *out) {
-  if (!hidden || !lm_head || (need_stats && !stats)) return SD_EINVAL;
+  if (!hidden || (!lm_head && !w12) || (need_stats && !stats)) return SD_EINVAL;
+  if (w12) {
+    if (!w12->codes || !w12->corr) return SD_EINVAL;
+    if (w12->b2 < 1 || w12->b2 > 121) return SD_EINVAL;
+    // The W12 stream is read by the skinny contraction only.
+    if (d % 128 != 0 || (int64_t)B * (gamma + 1) > 64 || w12->cap < 4 || w12->cap % 4 != 0 ||
+        w12->cap > kW12MaxCap)
+      return SD_ESHAPE;
+    if (!aligned(w12->codes, 16) || !aligned(w12->corr, 16)) return SD_EALIGN;
+  }
   if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
   if (!isfinite(temperature) || temperature < 0.f) return SD_EINVAL;
   const int32_t sz = check_sizes(B, gamma, d, V);
   if (sz != SD_OK) return sz;
-  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || (stats && !aligned(stats, 8)) ||
+  if (!aligned(hidden, 16) || (lm_head && !aligned(lm_head, 16)) || (stats && !aligned(stats, 8)) ||
       (logits && !aligned(logits, 16)) || (draft_tokens && !aligned(draft_tokens, 4)) ||
       (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
     return SD_EALIGN;
@@ -149,7 +158,18 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head,
   char *wsb = reinterpret_cast<char *>(workspace);
   VerifyArgs &a = *out;
   a.hidden = hidden;
-  a.W = lm_head;
+  a.W = w12 ? nullptr : lm_head;
+  a.w12_codes = w12 ? w12->codes : nullptr;
+  a.w12_corr = w12 ? w12->corr : nullptr;
+  a.w12_cap = w12 ? w12->cap : 0;
+  a.w12_lut0 = a.w12_lut1 = 0u;
+  if (w12) {
+    // High byte of code t (sign clear): 0 for t = 0, b2 + t - 1 otherwise.
+    for (int t = 1; t < 8; ++t) {
+      const uint32_t hb = (uint32_t)(w12->b2 + t - 1) << (8 * (t & 3));
+      if (t < 4) a.w12_lut0 |= hb; else a.w12_lut1 |= hb;
+    }
+  }
   a.draft_tokens = draft_tokens;
   a.verify_len = verify_len;
   a.rm = RowMap{row_offsets, B, gamma};
@@ -175,8 +195,8 @@ int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
                          int32_t V, float temperature, float *logits, sd_row_stats *stats,
                          void *workspace, size_t workspace_bytes, void *stream) {
   VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma,
-                                  d, V, temperature, logits, stats, true, workspace,
+  const int32_t st = verify_setup(hidden, lm_head, nullptr, draft_tokens, verify_len, row_offsets,
+                                  B, gamma, d, V, temperature, logits, stats, true, workspace,
                                   workspace_bytes, &a);
   if (st != SD_OK) return st;
   return launch_status(launch_verify(a, (hipStream_t)stream));
@@ -188,8 +208,8 @@ int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
                               float *logits, void *workspace, size_t workspace_bytes,
                               void *stream) {
   VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, nullptr, verify_len, row_offsets, B, gamma, d,
-                                  V, temperature, logits, nullptr, false, workspace,
+  const int32_t st = verify_setup(hidden, lm_head, nullptr, nullptr, verify_len, row_offsets, B,
+                                  gamma, d, V, temperature, logits, nullptr, false, workspace,
                                   workspace_bytes, &a);
   if (st != SD_OK) return st;
   int n_part = 0;
@@ -207,8 +227,57 @@ int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
   if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
     return SD_EALIGN;
   VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma,
-                                  d, V, 0.f, nullptr, stats, true, workspace, workspace_bytes, &a);
+  const int32_t st = verify_setup(hidden, lm_head, nullptr, draft_tokens, verify_len, row_offsets,
+                                  B, gamma, d, V, 0.f, nullptr, stats, true, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
+                                            (hipStream_t)stream));
+}
+
+int32_t sd_verify_logits_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                             const int32_t *draft_tokens, const int32_t *verify_len,
+                             const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                             int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!lm_head) return SD_EINVAL;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, nullptr, lm_head, draft_tokens, verify_len, row_offsets,
+                                  B, gamma, d, V, temperature, logits, stats, true, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  return launch_status(launch_verify(a, (hipStream_t)stream));
+}
+
+int32_t sd_verify_contraction_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                                  const int32_t *verify_len, const int32_t *row_offsets, int32_t B,
+                                  int32_t gamma, int32_t d, int32_t V, float temperature,
+                                  float *logits, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  if (!lm_head) return SD_EINVAL;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, nullptr, lm_head, nullptr, verify_len, row_offsets, B,
+                                  gamma, d, V, temperature, logits, nullptr, false, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  int n_part = 0;
+  bool zx_done = false;
+  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part, &zx_done));
+}
+
+int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                             const int32_t *draft_tokens, const int32_t *verify_len,
+                             const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                             int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                             int32_t *next_token, int64_t *counters, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  if (!lm_head || !draft_tokens || !accept_len || !next_token) return SD_EINVAL;
+  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
+    return SD_EALIGN;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, nullptr, lm_head, draft_tokens, verify_len, row_offsets,
+                                  B, gamma, d, V, 0.f, nullptr, stats, true, workspace,
+                                  workspace_bytes, &a);
   if (st != SD_OK) return st;
   return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
                                             (hipStream_t)stream));

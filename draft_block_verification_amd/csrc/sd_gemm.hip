@@ -274,6 +274,70 @@ __global__ __launch_bounds__(256) void k_gemm_stream(VerifyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- W12 decoding
+// Eight bf16 weights of one W12 group (12 bytes: l0, l1 the low bytes of columns 0-3
+// and 4-7, n the eight 4-bit codes, column j in bits 4j..4j+3). A code holds the sign
+// in bit 3 and t in bits 0-2; the high byte is sign << 7 | lut[t], looked up four at a
+// time with one byte permute (lut0 / lut1: the high bytes of t = 0..3 / 4..7), then
+// interleaved with the low bytes into bf16 pairs. SpecPilot page, "Reasons": the
+// weights travel as 4-bit planes and are rebuilt in the GEMM's registers.
+__device__ inline u32x4 w12_decode8(uint32_t l0, uint32_t l1, uint32_t n, uint32_t lut0,
+                                    uint32_t lut1) {
+  const uint32_t y = n & 0x0F0F0F0Fu, z = (n >> 4) & 0x0F0F0F0Fu;
+  const uint32_t x0 = __builtin_amdgcn_perm(z, y, 0x05010400u);   // codes of columns 0..3
+  const uint32_t x1 = __builtin_amdgcn_perm(z, y, 0x07030602u);   // columns 4..7
+  const uint32_t h0 = __builtin_amdgcn_perm(lut1, lut0, x0 & 0x07070707u) | ((x0 & 0x08080808u) << 4);
+  const uint32_t h1 = __builtin_amdgcn_perm(lut1, lut0, x1 & 0x07070707u) | ((x1 & 0x08080808u) << 4);
+  return u32x4{__builtin_amdgcn_perm(h0, l0, 0x05010400u), __builtin_amdgcn_perm(h0, l0, 0x07030602u),
+               __builtin_amdgcn_perm(h1, l1, 0x05010400u), __builtin_amdgcn_perm(h1, l1, 0x07030602u)};
+}
+
+// Byte offset of group c of LM-head row x in the region-blocked W12 layout.
+__device__ inline size_t w12_group_offset(int x, int c, int nst) {
+  return ((((size_t)(x >> 6) * nst + (c >> 4)) * 64 + (x & 63)) * 16 + (c & 15)) * 12;
+}
+
+// fp64 sum of h[k] * w[k] over eight bf16 pairs.
+__device__ inline double dot8_f64(const u32x4 &hv, const u32x4 &wv) {
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    part += (double)__uint_as_float(hv[e] << 16) * (double)__uint_as_float(wv[e] << 16);
+    part += (double)__uint_as_float(hv[e] & 0xffff0000u) * (double)__uint_as_float(wv[e] & 0xffff0000u);
+  }
+  return part;
+}
+
+// Part of the exact logit hidden . W[x] taken by thread t of nt: groups t, t + nt, ...
+// of the LM-head row (bf16, or W12 codes plus that row's corrections).
+__device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h, int x, int t,
+                                          int nt) {
+  const int ng = a.d / 8;
+  double part = 0.0;
+  if (!a.w12_codes) {
+    const uint16_t *w = a.W + (size_t)x * a.d;
+    for (int c = t; c < ng; c += nt)
+      part += dot8_f64(*reinterpret_cast<const u32x4 *>(h + 8 * c),
+                       *reinterpret_cast<const u32x4 *>(w + 8 * c));
+    return part;
+  }
+  const int nst = a.d / 128, rl = x & 63;
+  for (int c = t; c < ng; c += nt) {
+    const uint32_t *g = reinterpret_cast<const uint32_t *>(a.w12_codes + w12_group_offset(x, c, nst));
+    part += dot8_f64(*reinterpret_cast<const u32x4 *>(h + 8 * c),
+                     w12_decode8(g[0], g[1], g[2], a.w12_lut0, a.w12_lut1));
+  }
+  for (int s = t; s < nst; s += nt) {
+    const uint32_t *slot = a.w12_corr + ((size_t)(x >> 6) * nst + s) * a.w12_cap;
+    for (int e = 0; e < a.w12_cap; ++e) {
+      const uint32_t ent = slot[e];
+      if (ent != 0u && (int)((ent >> 7) & 63u) == rl)
+        part += (double)bf16_to_f32(h[128 * s + (ent & 127u)]) * (double)__uint_as_float(ent & 0xffff0000u);
+    }
+  }
+  return part;
+}
+
 // ------------------------------------------------- streaming regime, direct to LDS
 // The streaming kernel for d % KC == 0. global_load_lds_dwordx4 moves every wave
 // load's 1 KB (four 256-byte row segments for KC = 128) straight into one of NS LDS
@@ -286,16 +350,28 @@ __global__ __launch_bounds__(256) void k_gemm_stream(VerifyArgs a) {
 // once. Workgroup g walks the k stages of a slab starting at stage (g * kstride) mod
 // nst (kstride coprime to nst), so concurrent workgroups read different offsets of
 // their rows instead of all hitting the same column of power-of-two-strided rows.
-template <int MT, int KC, int NS>
+//
+// With W12 the LM-head part of a stage is the slab's 64 rows of 12-byte groups (192
+// bytes per row, stored in order) followed by the stage's correction slots; each
+// fragment is decoded right before its MFMA, and the lanes owning a corrected weight's
+// column add hidden * weight to their accumulators after the stage's MFMAs.
+template <int MT, int KC, int NS, bool W12>
 __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) {
   constexpr int BN = 64;
-  constexpr int CH = KC / 8;                 // 16-byte chunks per stage row
-  constexpr int RPI = 64 / CH;               // stage rows per wave instruction
-  constexpr int ROWS = BN + 16 * MT;         // LM-head rows, then hidden rows
-  constexpr int STAGE = ROWS * KC;           // bf16 per stage buffer
-  constexpr int DPT = ROWS * CH / 256;       // wave instructions per wave per stage
+  constexpr int CH = KC / 8;                 // 16-byte chunks per bf16 stage row
+  constexpr int RPI = 64 / CH;               // bf16 stage rows per wave instruction
+  static_assert(CH == 16, "stage shape");
+  // Stage layout in bytes: LM-head part, correction slots (W12), hidden rows.
+  constexpr int WBYTES = W12 ? BN * KC * 3 / 2 : BN * KC * 2;
+  constexpr int CBYTES = W12 ? 4 * kW12MaxCap : 0;
+  constexpr int HOFF = WBYTES + CBYTES;
+  constexpr int STAGE = (HOFF + 16 * MT * KC * 2) / 2;   // bf16 units per stage buffer
+  constexpr int WI = WBYTES / (16 * 256);    // LM-head wave instructions per wave
+  constexpr int CI = W12 ? 1 : 0;            // correction-slot instruction per wave
+  constexpr int HI = MT;                     // hidden wave instructions per wave
+  constexpr int DPT = WI + CI + HI;
   constexpr int PEND = (NS - 2) * DPT;       // loads allowed in flight past the oldest stage
-  static_assert(CH >= 16 && CH <= 64 && ROWS % (4 * RPI) == 0, "stage shape");
+  static_assert(WBYTES % (16 * 256) == 0, "LM-head part fills whole loads");
   static_assert(PEND < 64, "vmcnt holds 6 bits");
   __shared__ __attribute__((aligned(16))) uint16_t S[NS * STAGE];
 
@@ -304,31 +380,34 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   const int M = rows_total(a.rm);
   const int d = a.d, V = a.V;
 
-  // Load i of this thread fills stage row r = RPI * (wave + 4 i) + lane / CH, stored
-  // chunk lane % CH. The first WI loads cover the LM-head rows (they move with the
-  // slab), the rest the hidden rows (fixed source).
-  constexpr int WI = BN / (4 * RPI);
-  static_assert(BN % (4 * RPI) == 0, "LM-head rows fill whole loads");
-  int w_row[WI], w_chunk[WI];
-  const uint16_t *h_src[DPT - WI];
+  // LM-head load i of this thread: bf16 rows r = RPI * (wave + 4 i) + lane / CH, stored
+  // chunk lane % CH (swizzled); W12 16-byte piece u = 64 (wave + 4 i) + lane of the
+  // slab's 12 KB, row u / 12. Hidden load j: rows RPI * (wave + 4 j) + lane / CH of the
+  // hidden part.
+  int w_row[WI], w_off[WI];
+  const uint16_t *h_src[HI];
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) {
-    const int r = RPI * (wave + 4 * i) + lane / CH;
-    const int chunk = 8 * ((lane % CH) ^ (r & 15));
-    if (i < WI) {
-      w_row[i] = r;
-      w_chunk[i] = chunk;
+  for (int i = 0; i < WI; ++i) {
+    if (W12) {
+      w_row[i] = 0;                           // the region is contiguous: piece u at 16 u
+      w_off[i] = 16 * (64 * (wave + 4 * i) + lane);
     } else {
-      const int m = r - BN;
-      const uint16_t *src = a.hidden + chunk;   // rows past M read row 0; never used
-      if (m < M) {
-        int rq, jj;
-        const int hr = hidden_row(a.rm, m, &rq, &jj);
-        if (hr >= 0) src += (size_t)hr * d;
-        else raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
-      }
-      h_src[i - WI] = src;
+      const int r = RPI * (wave + 4 * i) + lane / CH;
+      w_row[i] = r;
+      w_off[i] = 8 * ((lane % CH) ^ (r & 15));
     }
+  }
+#pragma unroll
+  for (int j = 0; j < HI; ++j) {
+    const int m = RPI * (wave + 4 * j) + lane / CH;
+    const uint16_t *src = a.hidden + 8 * ((lane % CH) ^ (m & 15));   // rows past M: row 0, unused
+    if (m < M) {
+      int rq, jj;
+      const int hr = hidden_row(a.rm, m, &rq, &jj);
+      if (hr >= 0) src += (size_t)hr * d;
+      else raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+    }
+    h_src[j] = src;
   }
 
   // Drafted token of packed row `lane` (M <= 16 MT <= 64), when the drafted-token
@@ -352,19 +431,29 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   const int nst = d / KC;
   const int total = ((nslab - g + G - 1) / G) * nst;   // (slab, stage) pairs of this workgroup
   const int kshift = (int)(((long long)g * kstride) % nst);
+  const int cap = W12 ? a.w12_cap : 0;
   auto issue = [&](int t) {
-    const int slab = g + (t / nst) * G, k0 = ((t + kshift) % nst) * KC;
-    LDSP uint16_t *dst = (LDSP uint16_t *)S + (t % NS) * STAGE;
+    const int slab = g + (t / nst) * G, st = (t + kshift) % nst, k0 = st * KC;
+    LDSP char *dst = (LDSP char *)S + (size_t)(t % NS) * STAGE * 2;
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      if (i < WI)
-        __builtin_amdgcn_global_load_lds(
-            (const GLBP void *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_chunk[i] + k0),
-            (LDSP void *)(dst + (wave + 4 * i) * 512), 16, 0, kCachePolicyStream);
-      else
-        __builtin_amdgcn_global_load_lds((const GLBP void *)(h_src[i - WI] + k0),
-                                         (LDSP void *)(dst + (wave + 4 * i) * 512), 16, 0, 0);
+    for (int i = 0; i < WI; ++i) {
+      const GLBP char *src = W12
+          ? (const GLBP char *)(a.w12_codes + ((size_t)slab * nst + st) * WBYTES + w_off[i])
+          : (const GLBP char *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_off[i] + k0);
+      __builtin_amdgcn_global_load_lds((const GLBP void *)src, (LDSP void *)(dst + (wave + 4 * i) * 1024),
+                                       16, 0, kCachePolicyStream);
     }
+    if (W12 && lane < 4) {
+      // Slots 16 (4 wave + lane) .. + 3 of this (slab, stage); past CAP, a repeat of the
+      // region's last 16 bytes (never read).
+      const int ch = min(4 * wave + lane, cap / 4 - 1);
+      const GLBP char *src = (const GLBP char *)(a.w12_corr + ((size_t)slab * nst + st) * cap) + 16 * ch;
+      __builtin_amdgcn_global_load_lds((const GLBP void *)src, (LDSP void *)(dst + WBYTES + 64 * wave), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < HI; ++j)
+      __builtin_amdgcn_global_load_lds((const GLBP void *)(h_src[j] + k0),
+                                       (LDSP void *)(dst + HOFF + (wave + 4 * j) * 1024), 16, 0, 0);
   };
 
   f32x4 acc[MT];
@@ -392,15 +481,48 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     lds_barrier();
     if (t + NS - 1 < total) issue(t + NS - 1);   // refills the buffer read in pair t - 1
     const LDSP uint16_t *Sb = (const LDSP uint16_t *)S + (t % NS) * STAGE;
+    const LDSP uint16_t *Hb = Sb + HOFF / 2;                     // hidden rows
+    const LDSP uint32_t *Wq = (const LDSP uint32_t *)Sb;          // W12 groups
+    const LDSP uint32_t *Cb = (const LDSP uint32_t *)(Sb + WBYTES / 2);   // correction slots
 #pragma unroll
     for (int s = 0; s < KC / 32; ++s) {
       const int c = 4 * s + fc;
-      const bf16x8 b = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + br * KC + 8 * (c ^ (br & 15))));
+      bf16x8 b;
+      if (W12) {
+        const int o = (br * KC * 3 / 2 + 12 * c) / 4;
+        b = __builtin_bit_cast(bf16x8, w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1));
+      } else {
+        b = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + br * KC + 8 * (c ^ (br & 15))));
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const int ar = BN + 16 * i + fr;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + ar * KC + 8 * (c ^ (ar & 15))));
+        const int hr = 16 * i + fr;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Hb + hr * KC + 8 * (c ^ (hr & 15))));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[i], 0, 0, 0);
+      }
+    }
+    // W12 correction slots of this stage: lane l holds slot l; a ballot picks the slots
+    // whose column this wave owns.
+    uint32_t cent = 0u;
+    unsigned long long cmask = 0ull;
+    if (W12) {
+      cent = lane < cap ? Cb[lane] : 0u;
+      cmask = __ballot(cent != 0u && (int)((cent >> 11) & 3u) == wave);   // row_local / 16
+      // Corrected weights: the four lanes owning the column add hidden[m][k] * w for
+      // their rows (exact products in fp32).
+      for (unsigned long long mm = cmask; mm; mm &= mm - 1) {
+        const uint32_t ent = (uint32_t)__shfl((int)cent, __ffsll((long long)mm) - 1);
+        if ((int)((ent >> 7) & 15u) == fr) {
+          const int kl = ent & 127u;
+          const float wv = __uint_as_float(ent & 0xffff0000u);
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int m = 16 * i + 4 * fc + q;
+              acc[i][q] = fmaf(bf16_to_f32(Hb[m * KC + 8 * ((kl >> 3) ^ (m & 15)) + (kl & 7)]), wv, acc[i][q]);
+            }
+        }
       }
     }
     if (t % nst == 0) {
@@ -413,15 +535,27 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
       zw = __shfl(ztok, zrow >= 0 ? zrow : 0) - slab * BN;
       zacc = 0.0;
     }
-    if (zrow >= 0 && lane < CH) {
-      // Lane l takes logical chunk l (8 values) of the staged hidden and LM-head rows.
-      const int hrow = BN + zrow;
-      const u32x4 hv = *(const LDSP u32x4 *)(Sb + hrow * KC + 8 * (lane ^ (hrow & 15)));
-      const u32x4 wv = *(const LDSP u32x4 *)(Sb + zw * KC + 8 * (lane ^ (zw & 15)));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        zacc += (double)__uint_as_float(hv[e] << 16) * (double)__uint_as_float(wv[e] << 16);
-        zacc += (double)__uint_as_float(hv[e] & 0xffff0000u) * (double)__uint_as_float(wv[e] & 0xffff0000u);
+    if (zrow >= 0) {
+      // Lane l < CH takes logical chunk l (8 values) of the staged hidden and LM-head
+      // rows; with W12, lane 0 also adds the row's corrected weights of this stage.
+      if (lane < CH) {
+        const u32x4 hv = *(const LDSP u32x4 *)(Hb + zrow * KC + 8 * (lane ^ (zrow & 15)));
+        u32x4 wv;
+        if (W12) {
+          const int o = (zw * KC * 3 / 2 + 12 * lane) / 4;
+          wv = w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1);
+        } else {
+          wv = *(const LDSP u32x4 *)(Sb + zw * KC + 8 * (lane ^ (zw & 15)));
+        }
+        zacc += dot8_f64(hv, wv);
+      }
+      if (W12) {
+        // The row's corrected weights of this stage, one lane each.
+        if (cent != 0u && (int)((cent >> 7) & 63u) == zw) {
+          const int kl = cent & 127u;
+          zacc += (double)bf16_to_f32(Hb[zrow * KC + 8 * ((kl >> 3) ^ (zrow & 15)) + (kl & 7)]) *
+                  (double)__uint_as_float(cent & 0xffff0000u);
+        }
       }
     }
     if (t % nst == nst - 1) {
@@ -913,14 +1047,14 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
 #pragma unroll
   for (int i = 0; i < kDotPer; ++i) {
     const int c = tid + 256 * i;
-    hv[i] = need_dot && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    hv[i] = need_dot && !a.w12_codes && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
-  const uint16_t *wrow = a.W + (size_t)(has_x ? x : 0) * a.d;
+  const uint16_t *wrow = a.W ? a.W + (size_t)(has_x ? x : 0) * a.d : nullptr;
   u32x4 wv[kDotPer];
 #pragma unroll
   for (int i = 0; i < kDotPer; ++i) {
     const int c = tid + 256 * i;
-    wv[i] = need_dot && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    wv[i] = need_dot && !a.w12_codes && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
 
 #pragma unroll
@@ -956,17 +1090,14 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   double zd = has_x ? zg : 0.0;
   if (need_dot) {
     double part = 0.0;
-    auto dot8 = [&](const u32x4 &h, const u32x4 &w) {
+    if (a.w12_codes) {
+      part = lm_head_dot_part(a, hrow, x, tid, 256);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part += (double)__uint_as_float(h[e] << 16) * (double)__uint_as_float(w[e] << 16);
-        part += (double)__uint_as_float(h[e] & 0xffff0000u) * (double)__uint_as_float(w[e] & 0xffff0000u);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < kDotPer; ++i) dot8(hv[i], wv[i]);
-    for (int c = tid + 256 * kDotPer; c < nc; c += 256)
-      dot8(*reinterpret_cast<const u32x4 *>(hrow + 8 * c), *reinterpret_cast<const u32x4 *>(wrow + 8 * c));
+      for (int i = 0; i < kDotPer; ++i) part += dot8_f64(hv[i], wv[i]);
+      for (int c = tid + 256 * kDotPer; c < nc; c += 256)
+        part += dot8_f64(*reinterpret_cast<const u32x4 *>(hrow + 8 * c), *reinterpret_cast<const u32x4 *>(wrow + 8 * c));
+    }
     zd = block_sum(part, red);
   }
   if (tid == 0) write_stats(a, m, t1, t2, a1, lse, zd);
@@ -1024,27 +1155,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
     }
     const bool need_dot = has_x && (!a.zx || zg != zg);
     double part = 0.0;
-    if (need_dot) {
-      const uint16_t *h = a.hidden + ((size_t)r * (gamma + 1) + j) * a.d;
-      const uint16_t *w = a.W + (size_t)x * a.d;
-      for (int c0 = 0; c0 < nc; c0 += 64 * kFusedPer) {
-        u32x4 hv[kFusedPer], wv[kFusedPer];
-#pragma unroll
-        for (int i = 0; i < kFusedPer; ++i) {
-          const int c = c0 + lane + 64 * i;
-          hv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(h + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-          wv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(w + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < kFusedPer; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            part += (double)__uint_as_float(hv[i][e] << 16) * (double)__uint_as_float(wv[i][e] << 16);
-            part += (double)__uint_as_float(hv[i][e] & 0xffff0000u) *
-                    (double)__uint_as_float(wv[i][e] & 0xffff0000u);
-          }
-      }
-    }
+    if (need_dot)
+      part = lm_head_dot_part(a, a.hidden + ((size_t)r * (gamma + 1) + j) * a.d, x, lane, 64);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
@@ -1085,8 +1197,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
 // Resident workgroups per CU of each persistent kernel, cached for the current device.
 struct Occupancy {
   int device = -1, cus = 0;
-  const void *fn[8] = {};
-  int per_cu[8] = {};
+  const void *fn[16] = {};
+  int per_cu[16] = {};
 };
 Occupancy g_occ;
 
@@ -1100,11 +1212,11 @@ int resident_blocks(const void *fn) {
     g_occ.device = dev;
   }
   int slot = 0;
-  while (slot < 8 && g_occ.fn[slot] && g_occ.fn[slot] != fn) ++slot;
-  if (slot < 8 && g_occ.fn[slot] == fn) return g_occ.cus * g_occ.per_cu[slot];
+  while (slot < 16 && g_occ.fn[slot] && g_occ.fn[slot] != fn) ++slot;
+  if (slot < 16 && g_occ.fn[slot] == fn) return g_occ.cus * g_occ.per_cu[slot];
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess || n < 1) n = 1;
-  if (slot < 8) { g_occ.fn[slot] = fn; g_occ.per_cu[slot] = n; }
+  if (slot < 16) { g_occ.fn[slot] = fn; g_occ.per_cu[slot] = n; }
   return g_occ.cus * n;
 }
 
@@ -1136,14 +1248,20 @@ int stage_stride(int nst) {
   return 1;
 }
 
-template <int MT, int KC, int NS>
-hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
-  const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS>);
+template <int MT, int KC, int NS, bool W12>
+hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+  const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS, W12>);
   const int G = persistent_grid((a.V + 63) / 64, resident_blocks(fn), a.part_stride);
   *n_part = G;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS>), dim3(G), dim3(256), 0, stream, a,
+  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, W12>), dim3(G), dim3(256), 0, stream, a,
                      stage_stride(a.d / KC));
   return hipGetLastError();
+}
+
+template <int MT, int KC, int NS>
+hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+  return a.w12_codes ? launch_skinny_as<MT, KC, NS, true>(a, stream, n_part)
+                     : launch_skinny_as<MT, KC, NS, false>(a, stream, n_part);
 }
 
 }  // namespace

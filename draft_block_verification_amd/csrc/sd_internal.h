@@ -33,6 +33,9 @@ struct TilePartial {
 };
 static_assert(sizeof(TilePartial) == 16, "partials are 16 bytes");
 
+// Largest W12 correction-slot count per (64-row, 128-column) region the contraction stages.
+constexpr int kW12MaxCap = 64;
+
 // Smallest vocabulary tile used by any GEMM variant; sizes the partials array.
 constexpr int kMinVocabTile = 64;
 
@@ -112,6 +115,13 @@ struct VerifyArgs {
   int part_stride;
   double *zx;                   // [cap] drafted-token logits left by the contraction (NaN:
                                 // not computed there), or null when it leaves none
+  // W12 LM head (W null): region-blocked 12-byte groups [V/64][d/128][64][16][12],
+  // correction slots [V/64][d/128][cap], and the high bytes of codes t = 0..7 (sign
+  // clear) in two words: lut0 = t 0..3, lut1 = t 4..7. Null codes: W is bf16.
+  const uint8_t *w12_codes;
+  const uint32_t *w12_corr;
+  int w12_cap;
+  uint32_t w12_lut0, w12_lut1;
   sd_row_stats *stats;          // [cap]
   WsHeader *ws;
 };

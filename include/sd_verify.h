@@ -218,6 +218,70 @@ SD_API int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * W12 LM head (SpecPilot page, "Reasons": a lossless 12-bit weight format whose three
+ * 4-bit planes the GEMM rebuilds in registers). This library's layout:
+ *   - a bf16 weight's low byte (exponent bit 0, 7 mantissa bits) is kept verbatim;
+ *   - its high byte (sign, exponent bits 7..1 = e2) becomes the 4-bit code
+ *     sign << 3 | t: t = 0 for e2 = 0 (zeros, subnormals), t = e2 - b2 + 1 for e2 in
+ *     the tensor's window [b2, b2 + 6], b2 = max(1, largest nonzero e2 - 6);
+ *   - every other weight is coded as a signed zero and its exact bits go to a
+ *     correction slot of its region of 64 LM-head rows by 128 columns: uint32
+ *     k_local | row_local << 7 | bits << 16, sorted by (row_local, k_local), 0 = empty;
+ *   - a group of 8 columns 8 g .. 8 g + 7 of one row is 12 bytes: the 8 low bytes, then
+ *     byte 8 + i = code of column 8 g + 2 i | code of column 8 g + 2 i + 1 << 4; groups
+ *     are stored region by region, [ceil(V / 64)][d / 128][64 rows][16 groups][12 bytes],
+ *     rows past V zero (one region = one contiguous 12 KB block).
+ * Decoding gives back every bf16 bit pattern exactly.
+ */
+typedef struct sd_w12 {
+    const uint8_t *codes;    /* [ceil(V/64)][d/128][64][16][12], device, 16-byte aligned */
+    const uint32_t *corr;    /* [ceil(V / 64)][d / 128][cap] correction slots, device     */
+    int32_t cap;             /* slots per region: a multiple of 4 in [4, 64] for the GEMM */
+    int32_t b2;              /* window start, 1..121                                     */
+} sd_w12;
+
+/*
+ * Encode a bf16 LM head into W12 (host memory in and out; runs on the host).
+ *   W      bf16 [V][d] (d a multiple of 128)
+ *   codes  uint8 [ceil(V / 64)][d / 128][64][16][12] out (ignored by the sizing call)
+ *   corr   uint32 [ceil(V / 64)][d / 128][*cap] out, or NULL for the sizing call
+ *   cap    in: slots per region of corr; out: the slots needed (sizing call), or used
+ *   b2     out: window start
+ * A sizing call (corr NULL) sets *cap and *b2 only. SD_EWORKSPACE (with *cap set to
+ * the need) when *cap is too small; SD_ESHAPE for V < 1 or d not a positive multiple
+ * of 128.
+ */
+SD_API int32_t sd_w12_encode(const uint16_t *W, int32_t V, int32_t d, uint8_t *codes,
+                             uint32_t *corr, int32_t *cap, int32_t *b2);
+
+/*
+ * sd_verify_logits, sd_verify_contraction and sd_verify_greedy with the LM head
+ * given as W12 (lm_head:
+ * host struct of device pointers). The contraction decodes the 12-bit groups in
+ * registers and adds the corrected weights' products, so every result is that of
+ * the bf16 LM head (logits up to fp32 summation order). Restricted to the streaming
+ * regime: d % 128 == 0, B * (gamma + 1) <= 64 and cap <= 64, else SD_ESHAPE.
+ * Other arguments, outputs and errors as for the bf16 calls.
+ */
+SD_API int32_t sd_verify_logits_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                                    const int32_t *draft_tokens, const int32_t *verify_len,
+                                    const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                    int32_t d, int32_t V, float temperature, float *logits,
+                                    sd_row_stats *stats, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+SD_API int32_t sd_verify_contraction_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                                         const int32_t *verify_len, const int32_t *row_offsets,
+                                         int32_t B, int32_t gamma, int32_t d, int32_t V,
+                                         float temperature, float *logits, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+SD_API int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_head,
+                                    const int32_t *draft_tokens, const int32_t *verify_len,
+                                    const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                    int32_t d, int32_t V, sd_row_stats *stats,
+                                    int32_t *accept_len, int32_t *next_token, int64_t *counters,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Greedy acceptance (LFM2.5-DSpark blog, "Quality parity"): a_r = first j < L_r
  * with stats[row_offsets[r] + j].argmax != draft_tokens[r][j], else L_r; the
  * emitted token is the target argmax of row a_r (a correction when a_r < L_r,

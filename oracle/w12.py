@@ -27,7 +27,10 @@ trips and hand-computed bytes instead):
   k_local | row_local << 7 | bits << 16.
 * Bytes: each row is cut into groups of 8 consecutive columns, 12 bytes per
   group: bytes 0..7 are the 8 low bytes, and byte 8 + i holds the code of
-  column 2i (low nibble) and of column 2i + 1 (high nibble).
+  column 2i (low nibble) and of column 2i + 1 (high nibble). `codes` below is
+  indexed [row][group]; in device memory the groups are laid out by region,
+  [V/64][d/128][64 rows][16 groups][12 bytes] with rows past V zero
+  (device_layout), so each region the GEMM stages is one contiguous 12 KB block.
 
 Decoding a weight = its correction bits if it has one, else
 (sign << 15) | ((t ? b2 + t - 1 : 0) << 8) | low byte.
@@ -111,3 +114,14 @@ def decode(w: W12, V: int, d: int) -> np.ndarray:
                 k = j * COLS_PER_STAGE + (e & 0x7F)
                 bits[v, k] = e >> 16
     return bits
+
+
+def device_layout(codes: np.ndarray) -> np.ndarray:
+    """codes [V][d/8][12] -> [ceil(V/64)][d/128][64][16][12], rows past V zero."""
+    V, ng, _ = codes.shape
+    nslab = (V + ROWS_PER_SLAB - 1) // ROWS_PER_SLAB
+    pad = np.zeros((nslab * ROWS_PER_SLAB, ng, 12), dtype=np.uint8)
+    pad[:V] = codes
+    gps = COLS_PER_STAGE // GROUP
+    return np.ascontiguousarray(
+        pad.reshape(nslab, ROWS_PER_SLAB, ng // gps, gps, 12).transpose(0, 2, 1, 3, 4))

@@ -79,3 +79,15 @@ def test_correction_regions_and_order():
     assert [((e >> 7) & 0x3F, e & 0x7F) for e in first] == [(0, 3), (0, 5), (1, 3), (2, 0), (3, 1), (63, 127)]
     assert [int(e) & 0xFFFF for e in enc.corr[2, 1] if e] == [2 | 1 << 7, 72 | 1 << 7]
     assert np.array_equal(X.decode(enc, V, d), W)
+
+
+def test_device_layout_is_a_region_blocked_permutation():
+    V, d = 70, 256
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 256, (V, d // 8, 12)).astype(np.uint8)
+    dev = X.device_layout(codes)
+    assert dev.shape == (2, 2, 64, 16, 12)
+    # Row v, group c lives in region (v // 64, c // 16) at (v % 64, c % 16).
+    for v, c in [(0, 0), (5, 17), (63, 31), (64, 3), (69, 16)]:
+        assert np.array_equal(dev[v // 64, c // 16, v % 64, c % 16], codes[v, c])
+    assert not dev[1, :, 6:].any()                    # rows 70..127 are padding
