@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   constexpr int BN = 64;
   constexpr int CH = KC / 8;                 // 16-byte chunks per bf16 stage row
   constexpr int RPI = 64 / CH;               // bf16 stage rows per wave instruction
-  static_assert(CH == 16, "stage shape");
+  static_assert((CH == 16 || CH == 32) && (!W12 || KC == 128), "stage shape");
   // Stage layout in bytes: LM-head part, correction slots (W12), hidden rows.
   constexpr int WBYTES = W12 ? BN * KC * 3 / 2 : BN * KC * 2;
   constexpr int CBYTES = W12 ? 4 * kW12MaxCap : 0;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   constexpr int STAGE = (HOFF + 16 * MT * KC * 2) / 2;   // bf16 units per stage buffer
   constexpr int WI = WBYTES / (16 * 256);    // LM-head wave instructions per wave
   constexpr int CI = W12 ? 1 : 0;            // correction-slot instruction per wave
-  constexpr int HI = MT;                     // hidden wave instructions per wave
+  constexpr int HI = MT * KC / 128;          // hidden wave instructions per wave
   constexpr int DPT = WI + CI + HI;
   constexpr int PEND = (NS - 2) * DPT;       // loads allowed in flight past the oldest stage
   static_assert(WBYTES % (16 * 256) == 0, "LM-head part fills whole loads");
@@ -1260,8 +1260,10 @@ hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part
 
 template <int MT, int KC, int NS>
 hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
-  return a.w12_codes ? launch_skinny_as<MT, KC, NS, true>(a, stream, n_part)
-                     : launch_skinny_as<MT, KC, NS, false>(a, stream, n_part);
+  if constexpr (KC == 128) {
+    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, true>(a, stream, n_part);
+  }
+  return launch_skinny_as<MT, KC, NS, false>(a, stream, n_part);
 }
 
 }  // namespace
