@@ -73,6 +73,10 @@ SHAPES = [
     ("tiled-trunc-rej", 40, 16, 200, 5000, 1.0, True),
     ("gamma64", 2, 64, 64, 300, 1.0, False),
     ("many-requests", 300, 3, 64, 129, 0.0, True),
+    # Degenerate sizes: one vocabulary id, the smallest hidden size, one drafted token.
+    ("edge-d8-V1-rej", 1, 1, 8, 1, 1.0, False),
+    ("edge-gamma1-V5-greedy", 2, 1, 16, 5, 0.0, False),
+    ("edge-d8-V64-trunc", 4, 3, 8, 64, 0.7, True),
     # More vocabulary tiles than the chip holds at once (a second, partial round).
     ("tiled-two-rounds-rej", 5, 16, 64, 70000, 1.0, True),
     ("tiled-two-rounds-greedy", 4, 20, 128, 69999, 0.0, False),
