@@ -1194,30 +1194,34 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
   }
 }
 
-// Resident workgroups per CU of each persistent kernel, cached for the current device.
+// Resident workgroups per CU of each persistent kernel, cached per host thread for the
+// device current on it (recomputed when that device changes), so concurrent callers on
+// different threads never share the cache.
 struct Occupancy {
   int device = -1, cus = 0;
   const void *fn[16] = {};
   int per_cu[16] = {};
 };
-Occupancy g_occ;
+thread_local Occupancy t_occ;
 
 int resident_blocks(const void *fn) {
-  if (g_occ.device < 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (t_occ.device != dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 1;
-    g_occ.cus = cus > 0 ? cus : 1;
-    g_occ.device = dev;
+    t_occ = Occupancy{};
+    t_occ.cus = cus > 0 ? cus : 1;
+    t_occ.device = dev;
   }
   int slot = 0;
-  while (slot < 16 && g_occ.fn[slot] && g_occ.fn[slot] != fn) ++slot;
-  if (slot < 16 && g_occ.fn[slot] == fn) return g_occ.cus * g_occ.per_cu[slot];
+  while (slot < 16 && t_occ.fn[slot] && t_occ.fn[slot] != fn) ++slot;
+  if (slot < 16 && t_occ.fn[slot] == fn) return t_occ.cus * t_occ.per_cu[slot];
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess || n < 1) n = 1;
-  if (slot < 16) { g_occ.fn[slot] = fn; g_occ.per_cu[slot] = n; }
-  return g_occ.cus * n;
+  if (slot < 16) { t_occ.fn[slot] = fn; t_occ.per_cu[slot] = n; }
+  return t_occ.cus * n;
 }
 
 // Balanced persistent grid over BN-row slabs: at most one workgroup per resident slot
