@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--weights", choices=["bf16", "w12"], default="bf16",
                     help="LM-head format: bf16, or the lossless W12 stream (streaming regime "
                          "only; encoded on the host before timing)")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="instead of the verify benchmark: the toy multi-step decode loop "
+                         "(bigram target over the workload's LM head, drafter table right 75%% "
+                         "of the time) replayed from a HIP graph; reports emitted tokens/s")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB "
                          "(the known-size reference for the profiler's HBM byte counters)")
@@ -95,6 +99,8 @@ def main():
     from synth import make_step, make_weights, workload
 
     w = workload(args.workload)
+    if args.decode_loop:
+        return decode_loop_bench(args, w)
     K = args.steps if args.steps is not None else (1000 if w.name == "greedy-block9" else 50)
     Wu = args.warmup
     S = args.distinct or (w.steps if w.name in ("greedy-block9", "tiny-greedy") else 8)
@@ -305,6 +311,71 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def decode_loop_bench(args, w):
+    """Toy decode loop: greedy speculative decoding of a bigram target whose hidden state
+    is an embedding row planted toward a successor token's LM-head row; the drafter
+    proposes the target's choice 75% of the time. Steps are captured three at a time in a
+    HIP graph; the timed region replays it."""
+    import torch
+    import draft_block_verification_amd as sd
+    from draft_block_verification_amd.decode_loop import ToyDecodeLoop
+    from synth import make_weights
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = make_weights(w)
+    Wd = torch.from_numpy(np.ascontiguousarray(W).view(np.int16)).to(dev).view(torch.bfloat16)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    succ = torch.randperm(w.V, generator=gen).to(dev)
+    Wf = Wd[succ].float()
+    E = (0.3 * torch.randn((w.V, w.d), generator=gen).to(dev) / w.d ** 0.5 +
+         4.0 * Wf / Wf.norm(dim=1, keepdim=True)).to(torch.bfloat16)
+    del Wf
+    nxt = torch.empty(w.V, dtype=torch.int64, device=dev)
+    for v0 in range(0, w.V, 4096):                    # the target's greedy next token
+        nxt[v0:v0 + 4096] = (E[v0:v0 + 4096].float() @ Wd.float().T).argmax(1)
+    right = torch.rand(w.V, generator=gen).to(dev) < 0.75
+    dnext = torch.where(right, nxt, torch.randint(0, w.V, (w.V,), generator=gen).to(dev))
+    dconf = torch.where(right, torch.full((w.V,), 0.92, device=dev),
+                        0.2 + 0.4 * torch.rand(w.V, generator=gen).to(dev))
+    B, g = max(w.B, 8), w.gamma
+    reps = max(1, (args.steps or 300) // 3)
+    loop = ToyDecodeLoop(Wd, E, dnext, dconf, B, g, 3 * (reps + 1))
+    start = torch.randint(0, w.V, (B,), generator=gen).to(dev)
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        loop.reset(start)
+        for i in range(3):
+            loop.step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        for i in range(3):
+            loop.step(i)
+    with torch.cuda.stream(s):
+        loop.reset(start)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    emitted = int((loop.length - 1).sum().item())
+    drafted, accepted = loop.vr.counters.cpu().tolist()
+    out = {"metric": "toy decode loop emitted tokens/s (greedy speculative decoding, 1 GPU)",
+           "value": emitted / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": 3 * reps,
+           "ms_per_step": ms / (3 * reps), "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"decode-loop-{w.name}", "B": B, "gamma": g, "d": w.d, "V": w.V,
+                      "drafted": drafted, "accepted": accepted,
+                      "tokens_per_request_step": emitted / (3 * reps * B),
+                      "launch": "hipgraph (3 steps per graph)"}}
     print(json.dumps(out), flush=True)
 
 
