@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--weights", choices=["bf16", "w12"], default="bf16",
                     help="LM-head format: bf16, or the lossless W12 stream (streaming regime "
                          "only; encoded on the host before timing)")
+    ap.add_argument("--overlap", choices=["on", "off"], default="off",
+                    help="T > 0: run the drafter-row normaliser on a second stream beside the "
+                         "contraction (sd_draft_normalizer + sd_accept_rejection_prenormalized); "
+                         "measured 0.6-5%% slower on the rejection workloads, so off by default")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the verify benchmark: the toy multi-step decode loop "
                          "(bigram target over the workload's LM head, drafter table right 75%% "
@@ -147,7 +151,8 @@ def main():
         sched = sd.SCHED_EARLY_STOP if args.scheduler == "early-stop" else sd.SCHED_TOP_K
         sps = sd.profile_sps(w.B, w.gamma, W_dev[0], w.T)
     vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev,
-                        accept_rate=args.accept_rate, scheduler=sched, sps=sps)
+                        accept_rate=args.accept_rate, scheduler=sched, sps=sps,
+                        overlap=args.overlap == "on")
     stream = torch.cuda.Stream(device=dev)
 
     # The threshold reads survival confidences; the scheduler reads the conditional ones
@@ -302,6 +307,7 @@ def main():
                    "lm_head_copies": n_copies, "mean_rows": mean_rows,
                    "launch": "eager" if args.eager else "hipgraph",
                    "accept_rate": vr.accept_rate is not None,
+                   "overlap": vr.side is not None,
                    "scheduler": args.scheduler,
                    "lm_head_format": args.weights,
                    # Expected tokens per second if the confidences are calibrated survival

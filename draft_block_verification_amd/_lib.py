@@ -52,6 +52,10 @@ _SIGS = {
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_accept_rejection_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sd_draft_normalizer": (_i32, [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "sd_accept_rejection_prenormalized": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                 _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                 _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -458,6 +462,41 @@ def sd_accept_rejection_ex(logits: torch.Tensor, stats: torch.Tensor, draft_logi
                              accept_len, next_token, counters, accept_rate, workspace, stream)
 
 
+def sd_draft_normalizer(draft_logits: torch.Tensor, verify_len: Optional[torch.Tensor],
+                        temperature: float, workspace: torch.Tensor, stream=None) -> None:
+    """Drafter-row normaliser alone, into the accept workspace (see
+    sd_accept_rejection_prenormalized); independent of the verify outputs."""
+    _need(draft_logits, "draft_logits", torch.bfloat16)
+    B, g, V = draft_logits.shape
+    if verify_len is not None:
+        _need(verify_len, "verify_len", torch.int32, (B,))
+    _need(workspace, "workspace", torch.uint8)
+    _check("sd_draft_normalizer",
+           _lib.sd_draft_normalizer(_ptr(draft_logits), _ptr(verify_len), B, g, V,
+                                    float(temperature), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
+
+
+def sd_accept_rejection_prenormalized(logits: torch.Tensor, stats: torch.Tensor,
+                                      draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                                      verify_len: Optional[torch.Tensor],
+                                      row_offsets: Optional[torch.Tensor], u_accept: torch.Tensor,
+                                      u_resample: torch.Tensor, temperature: float,
+                                      accept_len: Optional[torch.Tensor] = None,
+                                      next_token: Optional[torch.Tensor] = None,
+                                      counters: Optional[torch.Tensor] = None,
+                                      accept_rate: Optional[torch.Tensor] = None,
+                                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """sd_accept_rejection_ex after sd_draft_normalizer wrote this workspace (accept_rate
+    may stay None here)."""
+    if workspace is None:
+        raise ValueError("the workspace sd_draft_normalizer filled is required")
+    return _accept_rejection("sd_accept_rejection_prenormalized", logits, stats, draft_logits,
+                             draft_tokens, verify_len, row_offsets, u_accept, u_resample,
+                             temperature, accept_len, next_token, counters, accept_rate,
+                             workspace, stream)
+
+
 def _accept_rejection(name, logits, stats, draft_logits, draft_tokens, verify_len, row_offsets,
                       u_accept, u_resample, temperature, accept_len, next_token, counters,
                       accept_rate, workspace, stream):
@@ -483,6 +522,10 @@ def _accept_rejection(name, logits, stats, draft_logits, draft_tokens, verify_le
     if name == "sd_accept_rejection_ex":
         _need(accept_rate, "accept_rate", torch.float64, (B, g))
         args.append(_ptr(accept_rate))
+    elif name == "sd_accept_rejection_prenormalized":
+        if accept_rate is not None:
+            _need(accept_rate, "accept_rate", torch.float64, (B, g))
+        args.append(_ptr(accept_rate))
     args += [_ptr(workspace), workspace.numel(), _stream(stream)]
     _check(name, getattr(_lib, name)(*args))
     return accept_len, next_token, accept_rate
@@ -496,13 +539,16 @@ class VerifyRound:
     truncate -> verify logits -> accept (greedy when temperature == 0, else rejection),
     all on one stream with no host synchronisation. At temperature 0 the verify and
     accept steps run through sd_verify_greedy (one launch fewer); fused=False keeps
-    the separate sd_verify_logits + sd_accept_greedy calls.
+    the separate sd_verify_logits + sd_accept_greedy calls. With overlap=True (T > 0)
+    the drafter-row normaliser runs on a second stream beside sd_verify_logits (it
+    needs only the kept lengths), joined before sd_accept_rejection_prenormalized; the
+    fork and join are stream waits, so the round still captures into one graph.
     """
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
                  truncate: bool, threshold: float = 0.3, device="cuda", stream=None,
                  fused: bool = True, accept_rate: bool = False, scheduler: Optional[int] = None,
-                 sps: Optional[torch.Tensor] = None):
+                 sps: Optional[torch.Tensor] = None, overlap: bool = False):
         self.B, self.gamma, self.d, self.V = B, gamma, d, V
         # With a scheduler mode (SCHED_EARLY_STOP / SCHED_TOP_K) and an SPS table, the
         # prefix scheduler replaces the confidence threshold.
@@ -527,6 +573,7 @@ class VerifyRound:
         # Analytic acceptance rate per verified draft position (rejection rounds only).
         self.accept_rate = (torch.empty((B, gamma), dtype=torch.float64, device=dev)
                             if accept_rate and self.T > 0 else None)
+        self.side = torch.cuda.Stream(device=dev) if overlap and self.T > 0 else None
 
     def run(self, hidden, lm_head, draft_tokens, conf=None, draft_logits=None, u_accept=None,
             u_resample=None, stream=None, conf_stale=None):
@@ -541,6 +588,19 @@ class VerifyRound:
             sd_verify_greedy(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                              self.stats, self.accept_len, self.next_token, self.counters,
                              self.ws_verify, stream=stream)
+            return self.accept_len, self.next_token
+        if self.side is not None:
+            main = stream if stream is not None else torch.cuda.current_stream()
+            self.side.wait_stream(main)                       # kept lengths are ready
+            sd_draft_normalizer(draft_logits, self.verify_len, self.T, self.ws_accept,
+                                stream=self.side)
+            sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
+                             self.T, self.logits, self.stats, self.ws_verify, stream=main)
+            main.wait_stream(self.side)
+            sd_accept_rejection_prenormalized(
+                self.logits, self.stats, draft_logits, draft_tokens, self.verify_len,
+                self.row_offsets, u_accept, u_resample, self.T, self.accept_len, self.next_token,
+                self.counters, self.accept_rate, self.ws_accept, stream=main)
             return self.accept_len, self.next_token
         sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                          self.T, self.logits, self.stats, self.ws_verify, stream=stream)

@@ -639,48 +639,71 @@ size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay) {
   return total;
 }
 
+namespace {
+
+// Arguments of the rejection kernels; the workspace regions come from the layout.
+RejArgs rej_args(const uint16_t *draft_logits, const int32_t *verify_len, const RowMap &rm, int V,
+                 float temperature, void *workspace) {
+  AcceptLayout l;
+  accept_workspace_layout(rm.B, rm.gamma, V, &l);
+  char *w = reinterpret_cast<char *>(workspace);
+  RejArgs a{};
+  a.draft_logits = draft_logits;
+  a.verify_len = verify_len;
+  a.rm = rm;
+  a.V = V;
+  a.C = l.chunks;
+  a.sl = (float)(kLog2e / (double)temperature);
+  a.invT = 1.0 / (double)temperature;
+  a.lse_q = reinterpret_cast<double *>(w + l.lse_q);
+  a.acc_a = reinterpret_cast<int32_t *>(w + l.acc_a);
+  a.dpart = reinterpret_cast<DraftPart *>(w + l.dpart);
+  a.csum = reinterpret_cast<double *>(w + l.csum);
+  a.ws = reinterpret_cast<WsHeader *>(workspace);
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
+                                   int B, int gamma, int V, float temperature, void *workspace,
+                                   hipStream_t stream) {
+  const RowMap rm{nullptr, B, gamma};
+  const RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
+  hipLaunchKernelGGL(k_draft_partial, dim3(a.C, grid_rows(B * gamma)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
                                    const uint16_t *draft_logits, const int32_t *draft_tokens,
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
                                    int64_t *counters, double *accept_rate, void *workspace,
-                                   hipStream_t stream) {
-  AcceptLayout l;
-  accept_workspace_layout(rm.B, rm.gamma, V, &l);
-  char *w = reinterpret_cast<char *>(workspace);
-  RejArgs a;
+                                   bool normalized, hipStream_t stream) {
+  RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
   a.logits = logits;
   a.stats = stats;
-  a.draft_logits = draft_logits;
   a.draft_tokens = draft_tokens;
-  a.verify_len = verify_len;
-  a.rm = rm;
   a.u_accept = u_accept;
   a.u_resample = u_resample;
-  a.V = V;
-  a.C = l.chunks;
-  a.sl = (float)(kLog2e / (double)temperature);
-  a.invT = 1.0 / (double)temperature;
   a.accept_len = accept_len;
   a.next_token = next_token;
   a.counters = counters;
-  a.lse_q = reinterpret_cast<double *>(w + l.lse_q);
-  a.acc_a = reinterpret_cast<int32_t *>(w + l.acc_a);
-  a.dpart = reinterpret_cast<DraftPart *>(w + l.dpart);
-  a.csum = reinterpret_cast<double *>(w + l.csum);
   // The drafter chunk partials are dead after k_accept_decide; their storage
   // ([B][gamma][C] entries of 16 bytes) holds the rate chunk sums.
-  a.rate_part = accept_rate ? reinterpret_cast<double *>(w + l.dpart) : nullptr;
+  a.rate_part = accept_rate ? reinterpret_cast<double *>(a.dpart) : nullptr;
   a.rate = accept_rate;
-  a.ws = reinterpret_cast<WsHeader *>(workspace);
-  hipLaunchKernelGGL(k_draft_partial, dim3(l.chunks, grid_rows(rm.B * rm.gamma)), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!normalized) {
+    hipLaunchKernelGGL(k_draft_partial, dim3(a.C, grid_rows(rm.B * rm.gamma)), dim3(256), 0,
+                       stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int draw_rows = rm.B + (accept_rate ? rm.B * rm.gamma : 0);
-  hipLaunchKernelGGL(k_draw_partial, dim3(l.chunks, grid_rows(draw_rows)), dim3(256), 0, stream, a,
+  hipLaunchKernelGGL(k_draw_partial, dim3(a.C, grid_rows(draw_rows)), dim3(256), 0, stream, a,
                      draw_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_draw_finalize, dim3(rm.B), dim3(256), 0, stream, a);

@@ -337,7 +337,47 @@ int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
   return launch_status(launch_accept_rejection(logits, stats, draft_logits, draft_tokens,
                                                verify_len, rm, u_accept, u_resample, V,
                                                temperature, accept_len, next_token, counters,
-                                               accept_rate, workspace, (hipStream_t)stream));
+                                               accept_rate, workspace, false, (hipStream_t)stream));
+}
+
+int32_t sd_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len, int32_t B,
+                            int32_t gamma, int32_t V, float temperature, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!draft_logits) return SD_EINVAL;
+  if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
+  if (check_sizes(B, gamma, 8, V) != SD_OK) return SD_ESHAPE;
+  if (!aligned(draft_logits, 16) || (verify_len && !aligned(verify_len, 4))) return SD_EALIGN;
+  if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
+  if (!aligned(workspace, 256)) return SD_EALIGN;
+  return launch_status(launch_draft_normalizer(draft_logits, verify_len, B, gamma, V, temperature,
+                                               workspace, (hipStream_t)stream));
+}
+
+int32_t sd_accept_rejection_prenormalized(
+    const float *logits, const sd_row_stats *stats, const uint16_t *draft_logits,
+    const int32_t *draft_tokens, const int32_t *verify_len, const int32_t *row_offsets,
+    const float *u_accept, const float *u_resample, int32_t B, int32_t gamma, int32_t V,
+    float temperature, int32_t *accept_len, int32_t *next_token, int64_t *counters,
+    double *accept_rate, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!logits || !stats || !draft_logits || !draft_tokens || !u_accept || !u_resample ||
+      !accept_len || !next_token)
+    return SD_EINVAL;
+  if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
+  if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
+  if (check_sizes(B, gamma, 8, V) != SD_OK) return SD_ESHAPE;
+  if (!aligned(logits, 16) || !aligned(stats, 8) || !aligned(draft_logits, 16) ||
+      !aligned(draft_tokens, 4) || !aligned(u_accept, 4) || !aligned(u_resample, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (accept_rate && !aligned(accept_rate, 8)) ||
+      (verify_len && (!aligned(verify_len, 4) || !aligned(row_offsets, 4))))
+    return SD_EALIGN;
+  if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
+  if (!aligned(workspace, 256)) return SD_EALIGN;
+  RowMap rm{row_offsets, B, gamma};
+  return launch_status(launch_accept_rejection(logits, stats, draft_logits, draft_tokens,
+                                               verify_len, rm, u_accept, u_resample, V,
+                                               temperature, accept_len, next_token, counters,
+                                               accept_rate, workspace, true, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -165,12 +165,17 @@ struct AcceptLayout {
 };
 size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay);
 
+// Rejection acceptance. With normalized = true the drafter chunk partials are taken as
+// already written to the workspace by launch_draft_normalizer for the same inputs.
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
                                    const uint16_t *draft_logits, const int32_t *draft_tokens,
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
                                    int64_t *counters, double *accept_rate, void *workspace,
+                                   bool normalized, hipStream_t stream);
+hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
+                                   int B, int gamma, int V, float temperature, void *workspace,
                                    hipStream_t stream);
 
 }  // namespace sdv

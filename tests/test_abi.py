@@ -120,6 +120,38 @@ def test_accept_rejection_ex_host_validation():
     assert r(*small_ws) == 4
 
 
+def test_draft_normalizer_and_prenormalized_host_validation():
+    n = lib.sd_draft_normalizer
+    args = [FAKE, None, 1, 4, 1024, ctypes.c_float(1.0), FAKE, ctypes.c_size_t(1 << 20), None]
+    bad = list(args)
+    bad[0] = None
+    assert n(*bad) == 1                               # drafter logits required
+    bad = list(args)
+    bad[5] = ctypes.c_float(float("nan"))
+    assert n(*bad) == 1
+    bad = list(args)
+    bad[3] = 65
+    assert n(*bad) == 2                               # gamma past 64
+    bad = list(args)
+    bad[1] = ctypes.c_void_p(0x10002)
+    assert n(*bad) == 3                               # verify_len not 4-byte aligned
+    bad = list(args)
+    bad[7] = ctypes.c_size_t(64)
+    assert n(*bad) == 4
+    r = lib.sd_accept_rejection_prenormalized
+    args = [FAKE] * 8 + [1, 4, 1024, ctypes.c_float(1.0)] + [FAKE, FAKE, None, None, FAKE,
+                                                             ctypes.c_size_t(1 << 20), None]
+    bad = list(args)
+    bad[4] = None                                     # verify_len without row_offsets
+    assert r(*bad) == 1
+    bad = list(args)
+    bad[15] = ctypes.c_void_p(0x10004)
+    assert r(*bad) == 3
+    bad = list(args)
+    bad[17] = ctypes.c_size_t(64)
+    assert r(*bad) == 4
+
+
 def test_schedule_prefix_host_validation():
     f = lib.sd_schedule_prefix
 

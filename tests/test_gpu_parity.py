@@ -351,3 +351,73 @@ def test_out_of_range_lengths_are_clamped_and_flagged():
     o = O.accept_greedy(np.argmax(z, axis=1), s.draft_tokens, L, offs)
     assert np.array_equal(acc.cpu().numpy(), o.accept_len)
     assert np.array_equal(nxt.cpu().numpy(), o.next_token)
+
+
+OVERLAP_CASES = [
+    # (name, B, gamma, d, V, T, truncate, accept_rate)
+    ("ovl-small", 2, 5, 64, 1001, 1.0, False, False),
+    ("ovl-ragged-rate", 12, 16, 128, 9000, 0.8, True, True),
+    ("ovl-ragged-b32", None, None, None, None, None, None, False),
+]
+
+
+@pytest.mark.parametrize("case", OVERLAP_CASES, ids=[c[0] for c in OVERLAP_CASES])
+def test_overlapped_normalizer_matches_single_stream(case):
+    """sd_draft_normalizer on a second stream beside sd_verify_logits, then
+    sd_accept_rejection_prenormalized: every output byte equals the single-stream
+    sd_accept_rejection(_ex) round, eagerly and on each replay of a captured graph."""
+    name, B, g, d, V, T, trunc, rate = case
+    if B is None:
+        w = workload("ragged-b32")
+    else:
+        w = workload("ragged-b32", B=B, gamma=g, d=d, V=V, T=T, truncate=trunc,
+                     geo_p=(0.2,), name=name)
+    W = make_weights(w)
+    W_dev = bf16_dev(W)
+    s = make_step(w, W, 0)
+    ds = upload_step(s)
+    ref = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, accept_rate=rate)
+    ovl = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, accept_rate=rate,
+                         overlap=True)
+    say(name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} rate={rate} eager")
+    g_ref = run_gpu(w, W_dev, ds, ref)
+    g_ovl = run_gpu(w, W_dev, ds, ovl)
+    assert g_ref.flags == 0 and g_ovl.flags == 0
+
+    def same(a, b):
+        assert np.array_equal(a.verify_len, b.verify_len)
+        assert np.array_equal(a.accept_len, b.accept_len)
+        assert np.array_equal(a.next_token, b.next_token)
+        assert np.array_equal(a.counters, b.counters)
+        # Drafter log-normalisers exist for kept positions only (j < L_r).
+        kept = np.arange(w.gamma)[None, :] < a.verify_len[:, None]
+        assert a.lse_q[kept].tobytes() == b.lse_q[kept].tobytes()
+        assert a.stats.tobytes() == b.stats.tobytes()
+
+    same(g_ref, g_ovl)
+    if rate:
+        assert ref.accept_rate.cpu().numpy().tobytes() == ovl.accept_rate.cpu().numpy().tobytes()
+    # The same round captured into one graph (fork and join are stream waits), replayed
+    # with host reads in between.
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        ovl.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf, ds.draft_logits, ds.u_accept,
+                ds.u_resample)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        ovl.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf, ds.draft_logits, ds.u_accept,
+                ds.u_resample)
+    for rep in range(3):
+        say(name, f"graph replay {rep}")
+        ovl.counters.zero_()
+        ovl.accept_len.fill_(-7)
+        ovl.next_token.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(ovl.accept_len.cpu().numpy(), g_ref.accept_len)
+        assert np.array_equal(ovl.next_token.cpu().numpy(), g_ref.next_token)
+        assert np.array_equal(ovl.counters.cpu().numpy(), g_ref.counters)
+        if rate:
+            assert (ref.accept_rate.cpu().numpy().tobytes() ==
+                    ovl.accept_rate.cpu().numpy().tobytes())
