@@ -68,6 +68,9 @@ def parse():
                     help="instead of the verify benchmark: the toy multi-step decode loop "
                          "(bigram target over the workload's LM head, drafter table right 75%% "
                          "of the time) replayed from a HIP graph; reports emitted tokens/s")
+    ap.add_argument("--step-times-from-trace", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="no GPU run: read a rocprofv3 kernel trace of a bench.py run and print "
+                         "the median and p10/p90 of the per-step times of its first timed region")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB "
                          "(the known-size reference for the profiler's HBM byte counters)")
@@ -91,8 +94,37 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def step_times_from_trace(path):
+    """Per-step times of the first timed region in a rocprofv3 kernel trace of bench.py.
+
+    The timed region lies between the first two marker kernels (torch's spin kernel).
+    A step starts with the first kernel of the path (truncation or scheduling when the
+    workload truncates, else the contraction); a step's time runs from its first
+    kernel's start to the next step's, and for the last step to its last kernel's end.
+    """
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    marks = [i for i, r in enumerate(rows) if "spin" in r["Kernel_Name"].lower()]
+    if len(marks) < 2:
+        sys.exit("no pair of marker kernels in the trace")
+    region = rows[marks[0] + 1:marks[1]]
+    names = [r["Kernel_Name"] for r in region]
+    first = next((k for k in ("k_truncate", "k_schedule") if any(k in n for n in names)), "k_gemm")
+    starts = [i for i, n in enumerate(names) if first in n]
+    t = [int(region[i]["Start_Timestamp"]) for i in starts]
+    t.append(max(int(r["End_Timestamp"]) for r in region))
+    per = np.diff(np.array(t, dtype=np.float64)) / 1e3
+    out = {"steps": len(per), "first_kernel": first, "median_us": float(np.median(per)),
+           "p10_us": float(np.percentile(per, 10)), "p90_us": float(np.percentile(per, 90)),
+           "mean_us": float(per.mean())}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.step_times_from_trace:
+        return step_times_from_trace(args.step_times_from_trace)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               "(the verify path is measured on one GPU's full-vocabulary share).", file=sys.stderr)
@@ -189,6 +221,9 @@ def main():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
+            # Marker kernels outside the events bracket the timed steps in a kernel
+            # trace (see --step-times-from-trace).
+            torch.cuda._sleep(1000)
             e0.record(stream)
             if graph is not None:
                 graph.replay()
@@ -196,6 +231,7 @@ def main():
                 for i in range(n):
                     fn(warm + i)
             e1.record(stream)
+            torch.cuda._sleep(1000)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 

@@ -13,7 +13,7 @@
 // from p.
 #include <math.h>
 
-#include "sd_internal.h"
+#include "sd_launch.h"
 
 namespace sdv {
 namespace {

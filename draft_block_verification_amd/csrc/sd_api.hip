@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "sd_internal.h"
+#include "sd_launch.h"
 
 using namespace sdv;
 

@@ -21,7 +21,7 @@
 // drafted token's logit is recomputed exactly as an fp64 dot of the bf16 inputs.
 #include <math.h>
 
-#include "sd_internal.h"
+#include "sd_launch.h"
 
 #define LDSP __attribute__((address_space(3)))
 #define GLBP __attribute__((address_space(1)))

@@ -20,7 +20,7 @@
 // admitted set is then every candidate above the K-th sorted survival plus, among
 // those equal to it, the first ones in (request, position) order; a block scan of the
 // per-request counts gives the row offsets.
-#include "sd_internal.h"
+#include "sd_launch.h"
 
 namespace sdv {
 namespace {

@@ -123,12 +123,12 @@ def test_workload_greedy_block9():
 
 def test_workload_rejection_b1():
     w = workload("rejection-b1")
-    full_case(w, steps=range(6))
+    full_case(w, steps=range(10))
 
 
 def test_workload_ragged_b32():
     w = workload("ragged-b32")
-    full_case(w, steps=range(2))
+    full_case(w, steps=range(4))
 
 
 def test_workload_concurrency_b128_sampled():

@@ -348,6 +348,48 @@ def test_rejection_is_lossless_chi2():
     assert abs(rate - want) < 4 * np.sqrt(want * (1 - want) / B)
 
 
+def test_rejection_multi_round_three_tokens_chi2():
+    """DSpark summary, "Problem definition": speculative sampling, round after round,
+    emits the target's own autoregressive distribution. Bigram target and drafter over
+    V = 3; rounds of gamma = 2 drafts (x ~ q) continue from the last emitted token until
+    three tokens are out; their 27-cell distribution must match
+    p(v0 | anchor) p(v1 | v0) p(v2 | v1) (chi-square, alpha = 1e-3)."""
+    rng = np.random.default_rng(77)
+    V, g, N = 3, 2, 40000
+    Zt = _bigram(rng, V, 1.2)
+    Zd = _bigram(rng, V, 1.2)
+    pt, qt = _softmax_rows(Zt), _softmax_rows(Zd)
+    W = bf16_round(np.eye(V, dtype=np.float32))
+    out = [[0] for _ in range(N)]                 # token 0 is the anchor
+    todo = np.arange(N)
+    while todo.size:
+        last = np.array([out[i][-1] for i in todo])
+        B = todo.size
+        x = np.zeros((B, g), np.int32)
+        prev = last.copy()
+        for j in range(g):
+            cdf = np.cumsum(qt[prev], axis=1)
+            x[:, j] = np.minimum((rng.random((B, 1)) > cdf).sum(1), V - 1)
+            prev = x[:, j]
+        prevs = np.concatenate([last[:, None], x], axis=1)
+        hidden = bf16_round(Zt[prevs].astype(np.float32))
+        dl = bf16_round(Zd[prevs[:, :g]].astype(np.float32))
+        ua = rng.random((B, g)).astype(np.float32)
+        ur = rng.random((B, g + 1)).astype(np.float32)
+        res = O.verify_step(hidden, W, x, 1.0, draft_logit_bits=dl, u_accept=ua, u_resample=ur)
+        for k, i in enumerate(todo):
+            a = int(res.accept.accept_len[k])
+            out[i] += [int(t) for t in x[k, :a]] + [int(res.accept.next_token[k])]
+        todo = np.array([i for i in todo if len(out[i]) < 4], dtype=np.int64)
+    cells = np.zeros(V ** 3)
+    for o in out:
+        cells[o[1] * 9 + o[2] * 3 + o[3]] += 1
+    want = np.array([pt[0, a] * pt[a, b] * pt[b, c]
+                     for a in range(V) for b in range(V) for c in range(V)])
+    assert abs(want.sum() - 1.0) < 1e-12
+    assert _chi2_p(cells, want) > 1e-3
+
+
 def test_rejection_equal_distributions_accept_everything():
     rng = np.random.default_rng(8)
     V, g, B = 5, 3, 3000
@@ -441,3 +483,96 @@ def test_rejection_hand_case_uniform_indexing():
     assert int(allacc.accept.accept_len[0]) == 2 and int(allacc.accept.next_token[0]) == 1
     assert not bool(allacc.diag.residual[0])
     assert list(allacc.accept.counters) == [2, 2]
+
+
+def _bisect_first_change(f, lo, hi, iters=56):
+    """f is monotone on [lo, hi] with f(lo) != f(hi): the boundary point (to ~1e-17)."""
+    flo = f(lo)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if f(mid) == flo:
+            lo = mid
+        else:
+            hi = mid
+    return hi
+
+
+@pytest.mark.parametrize("V,g,L,T,seed", [(3, 3, 3, 1.0, 5), (4, 2, 2, 0.7, 6), (3, 3, 2, 1.3, 7)])
+def test_rejection_output_distribution_closed_form(V, g, L, T, seed):
+    """Exact output distribution of the oracle's rejection step against the closed form.
+
+    DSpark summary, "Problem definition" (rejection sampling keeps the target's output
+    distribution exactly). Drafts x ~ q are enumerated exhaustively; the oracle's
+    dependence on each uniform is integrated piecewise, every acceptance threshold and
+    every inverse-CDF breakpoint located by bisection on the oracle's own outputs. The
+    result must equal
+      P(a = k, emitted s_0..s_k) = prod_{i<k} min(p_i(s_i), q_i(s_i))
+                                   * (max(0, p_k(s_k) - q_k(s_k)) if k < L else p_L(s_L))
+    to 1e-12, with p, q from scipy's softmax of the decoded logits.
+    """
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0.0, 1.2, (L + 1, V))                       # target logits, rows 0..L
+    dl = bf16_round(rng.normal(0.0, 1.2, (1, g, V)).astype(np.float32))
+    p = special.softmax(z / T, axis=1)
+    q = special.softmax(bf16_to_f32(dl[0]).astype(np.float64) / T, axis=1)
+    vlen = np.array([L], np.int32)
+    offs = np.array([0, L + 1], np.int32)
+
+    def run(x, ua, ur):
+        tok = np.zeros((1, g), np.int32)
+        tok[0, :L] = x
+        res, _ = O.accept_rejection(z, dl, tok, vlen, offs, np.asarray(ua, np.float64)[None],
+                                    np.asarray(ur, np.float64)[None], T)
+        return int(res.accept_len[0]), int(res.next_token[0])
+
+    top = 1.0 - 2.0 ** -53
+    got = {}
+    for code in range(V ** L):
+        x = [(code // V ** i) % V for i in range(L)]
+        px = float(np.prod([q[i, x[i]] for i in range(L)]))
+        # Acceptance threshold of each position: with every earlier uniform 0 (always
+        # kept), position j is kept for u < t_j and rejected for u >= t_j.
+        t = []
+        for j in range(L):
+            def kept(u, j=j):
+                ua = np.zeros(g)
+                ua[j] = u
+                return run(x, ua, np.full(g + 1, 0.5))[0] > j
+            t.append(1.0 if kept(top) else _bisect_first_change(kept, 0.0, top))
+            assert kept(0.0)
+        for k in range(L + 1):
+            ua = np.zeros(g)
+            if k < L:
+                if t[k] >= 1.0:
+                    continue                                    # position k is never rejected
+                ua[k] = 0.5 * (t[k] + 1.0)
+            weight = px * float(np.prod(t[:k])) * ((1.0 - t[k]) if k < L else 1.0)
+
+            def emitted(u, ua=ua, k=k):
+                ur = np.full(g + 1, 0.5)
+                ur[k] = u
+                a, v = run(x, ua, ur)
+                assert a == k
+                return v
+            u0 = 0.0
+            while True:                                         # the draw is non-decreasing in u
+                v = emitted(u0)
+                b = top if emitted(top) == v else _bisect_first_change(emitted, u0, top)
+                if b == top:
+                    b = 1.0
+                key = (k, tuple(x[:k]) + (v,))
+                got[key] = got.get(key, 0.0) + weight * (b - u0)
+                if b >= 1.0:
+                    break
+                u0 = b
+    want = {}
+    for k in range(L + 1):
+        for code in range(V ** (k + 1)):
+            s = [(code // V ** i) % V for i in range(k + 1)]
+            pr = float(np.prod([min(p[i, s[i]], q[i, s[i]]) for i in range(k)]))
+            pr *= max(0.0, p[k, s[k]] - q[k, s[k]]) if k < L else p[L, s[L]]
+            if pr > 0.0:
+                want[(k, tuple(s))] = pr
+    assert abs(sum(got.values()) - 1.0) < 1e-12
+    for key in set(got) | set(want):
+        assert abs(got.get(key, 0.0) - want.get(key, 0.0)) < 1e-12, key
