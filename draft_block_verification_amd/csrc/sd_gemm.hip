@@ -484,13 +484,35 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     const LDSP uint16_t *Hb = Sb + HOFF / 2;                     // hidden rows
     const LDSP uint32_t *Wq = (const LDSP uint32_t *)Sb;          // W12 groups
     const LDSP uint32_t *Cb = (const LDSP uint32_t *)(Sb + WBYTES / 2);   // correction slots
+    // W12 correction slots of this stage: lane l holds slot l; one ballot per k-step
+    // picks the slots in this wave's rows whose column falls in that k-step.
+    uint32_t cent = 0u;
+    unsigned long long cmask[KC / 32] = {};
+    if (W12) {
+      cent = lane < cap ? Cb[lane] : 0u;
+      const bool mine = cent != 0u && (int)((cent >> 11) & 3u) == wave;   // row_local / 16
+#pragma unroll
+      for (int s = 0; s < KC / 32; ++s) cmask[s] = __ballot(mine && (int)((cent >> 5) & 3u) == s);
+    }
 #pragma unroll
     for (int s = 0; s < KC / 32; ++s) {
       const int c = 4 * s + fc;
       bf16x8 b;
       if (W12) {
         const int o = (br * KC * 3 / 2 + 12 * c) / 4;
-        b = __builtin_bit_cast(bf16x8, w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1));
+        u32x4 w = w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1);
+        // A corrected weight is coded as a signed zero; the lane holding its row and
+        // 8-column chunk puts the exact bits in its place before the MFMA.
+        for (unsigned long long mm = cmask[s]; mm; mm &= mm - 1) {
+          const uint32_t ent = (uint32_t)__builtin_amdgcn_readlane((int)cent, __ffsll((long long)mm) - 1);
+          if ((int)((ent >> 7) & 15u) == fr && (int)((ent >> 3) & 15u) == c) {
+            const uint32_t q = (ent >> 1) & 3u, sh = (ent & 1u) * 16u;
+            const uint32_t keep = ~(0xFFFFu << sh), put = (ent >> 16) << sh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)i == q ? ((w[i] & keep) | put) : w[i];
+          }
+        }
+        b = __builtin_bit_cast(bf16x8, w);
       } else {
         b = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + br * KC + 8 * (c ^ (br & 15))));
       }
@@ -499,30 +521,6 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         const int hr = 16 * i + fr;
         const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Hb + hr * KC + 8 * (c ^ (hr & 15))));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[i], 0, 0, 0);
-      }
-    }
-    // W12 correction slots of this stage: lane l holds slot l; a ballot picks the slots
-    // whose column this wave owns.
-    uint32_t cent = 0u;
-    unsigned long long cmask = 0ull;
-    if (W12) {
-      cent = lane < cap ? Cb[lane] : 0u;
-      cmask = __ballot(cent != 0u && (int)((cent >> 11) & 3u) == wave);   // row_local / 16
-      // Corrected weights: the four lanes owning the column add hidden[m][k] * w for
-      // their rows (exact products in fp32).
-      for (unsigned long long mm = cmask; mm; mm &= mm - 1) {
-        const uint32_t ent = (uint32_t)__shfl((int)cent, __ffsll((long long)mm) - 1);
-        if ((int)((ent >> 7) & 15u) == fr) {
-          const int kl = ent & 127u;
-          const float wv = __uint_as_float(ent & 0xffff0000u);
-#pragma unroll
-          for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int m = 16 * i + 4 * fc + q;
-              acc[i][q] = fmaf(bf16_to_f32(Hb[m * KC + 8 * ((kl >> 3) ^ (m & 15)) + (kl & 7)]), wv, acc[i][q]);
-            }
-        }
       }
     }
     if (t % nst == 0) {
@@ -1127,7 +1125,6 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
     }
     return;
   }
-  const int nc = a.d / 8;
   for (int j = wave; j <= L; j += kFusedWaves) {
     const int m = base + j;
     // The drafted token, its logit from the contraction when that left one, and the
