@@ -108,6 +108,19 @@ def test_truncation_edge_thresholds():
         full_case(w, steps=range(2))
 
 
+@pytest.mark.parametrize("case", [("rows-past-grid-y-rej", 4200, 16, 64, 300, 1.0, True),
+                                  ("rows-past-grid-y-greedy", 4200, 16, 64, 300, 0.0, False)],
+                         ids=["rej-trunc", "greedy"])
+def test_rows_beyond_one_grid_dimension(case):
+    """4200 requests x 17 rows (71400 > 65535): the kernels whose grid y is capped at
+    65535 stride over the remaining rows."""
+    name, B, g, d, V, T, trunc = case
+    w = workload("ragged-b32", B=B, gamma=g, d=d, V=V, T=T, truncate=trunc,
+                 geo_p=(0.2,), name=name)
+    rep = full_case(w, steps=range(1))
+    assert rep.requests == B
+
+
 # ----------------------------------------------------------- named workloads
 
 def test_workload_tiny_greedy_all_steps():
@@ -287,6 +300,8 @@ RATE_CASES = [
     ("rate-ragged", 12, 16, 128, 9000, 0.8, True, 2),
     ("rate-gamma64", 2, 64, 64, 4099, 1.3, False, 1),
     ("rate-rejection-b1", None, None, None, None, None, None, 2),
+    # B + B * gamma = 71400 draw-kernel rows: grid y (capped at 65535) strides over them.
+    ("rate-rows-past-grid-y", 4200, 16, 64, 300, 1.0, True, 1),
 ]
 
 
