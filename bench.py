@@ -57,9 +57,11 @@ def parse():
                     help="truncating workloads: confidence threshold (default) or the "
                          "hardware-aware prefix scheduler on an SPS table profiled at start "
                          "(top-k sizes the batch from the confidences of two steps before)")
-    ap.add_argument("--weights", choices=["bf16", "w12"], default="bf16",
-                    help="LM-head format: bf16, or the lossless W12 stream (streaming regime "
-                         "only; encoded on the host before timing)")
+    ap.add_argument("--weights", choices=["bf16", "w12", "blocked"], default="bf16",
+                    help="LM-head format: bf16 [V][d]; the lossless W12 stream (encoded on the "
+                         "host before timing); or the same bf16 weights re-laid in 64x128 slab "
+                         "blocks (sd_lm_head_block, before timing). w12 and blocked: streaming "
+                         "regime only")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="T > 0: run the drafter-row normaliser on a second stream beside the "
                          "contraction (sd_draft_normalizer + sd_accept_rejection_prenormalized); "
@@ -153,6 +155,9 @@ def main():
         enc = sd.w12_encode(W)
         w_bytes = enc[0].nbytes + enc[1].nbytes
         make_head = lambda: sd.W12Weights(*enc, device=dev)
+    elif args.weights == "blocked":
+        w_bytes = W.nbytes                      # the same bf16 weights, re-laid in slab blocks
+        make_head = lambda: sd.BlockedWeights(bf16_dev(W))
     else:
         w_bytes = W.nbytes
         make_head = lambda: bf16_dev(W)

@@ -6,7 +6,7 @@ in the library's HIP kernels.
 """
 from ._lib import (EXPORTED, FLAG_NO_RESIDUAL, FLAG_ROW_OFFSETS, FLAG_VERIFY_LEN, LIB_PATH,
                    ROW_STATS_DTYPE, SCHED_EARLY_STOP, SCHED_MAX_CANDIDATES, SCHED_TOP_K, SdError,
-                   VerifyRound, W12Weights, abi_version, accept_workspace_bytes, device_flags, new_stats,
+                   BlockedWeights, VerifyRound, W12Weights, abi_version, accept_workspace_bytes, device_flags, new_stats,
                    new_workspace, profile_sps, sd_accept_greedy, sd_accept_rejection,
                    sd_accept_rejection_ex, sd_accept_rejection_prenormalized,
                    sd_draft_normalizer, sd_schedule_prefix, sd_truncate_by_confidence,
@@ -17,7 +17,7 @@ from ._lib import (EXPORTED, FLAG_NO_RESIDUAL, FLAG_ROW_OFFSETS, FLAG_VERIFY_LEN
 
 __all__ = ["EXPORTED", "FLAG_NO_RESIDUAL", "FLAG_ROW_OFFSETS", "FLAG_VERIFY_LEN", "LIB_PATH",
            "ROW_STATS_DTYPE", "SCHED_EARLY_STOP", "SCHED_MAX_CANDIDATES", "SCHED_TOP_K", "SdError",
-           "VerifyRound", "W12Weights", "abi_version", "accept_workspace_bytes", "device_flags", "new_stats",
+           "BlockedWeights", "VerifyRound", "W12Weights", "abi_version", "accept_workspace_bytes", "device_flags", "new_stats",
            "new_workspace", "profile_sps", "sd_accept_greedy", "sd_accept_rejection",
            "sd_accept_rejection_ex", "sd_accept_rejection_prenormalized", "sd_draft_normalizer",
            "sd_schedule_prefix", "sd_truncate_by_confidence",

@@ -43,6 +43,14 @@ _SIGS = {
                                     _vp, _vp, _sz, _vp]),
     "sd_verify_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                 _vp, _sz, _vp]),
+    "sd_lm_head_block_bytes": (_sz, [_i32, _i32]),
+    "sd_lm_head_block": (_i32, [_vp, _i32, _i32, _vp, _sz, _vp]),
+    "sd_verify_logits_blocked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp,
+                                        _vp, _vp, _sz, _vp]),
+    "sd_verify_contraction_blocked": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp,
+                                             _vp, _sz, _vp]),
+    "sd_verify_greedy_blocked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                        _vp, _vp, _vp, _sz, _vp]),
     "sd_verify_contraction": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
                                      _vp]),
     "sd_verify_greedy": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -299,16 +307,37 @@ def sd_verify_greedy_w12(hidden, lm_head: W12Weights, *args, **kwargs):
     return sd_verify_greedy(hidden, lm_head, *args, **kwargs)
 
 
+class BlockedWeights:
+    """A bf16 LM head re-laid once into slab blocks (sd_lm_head_block) so the streaming
+    contraction reads each stage as one contiguous 16 KB block. Same values as the
+    [V][d] tensor; pass it as `lm_head` to sd_verify_logits / sd_verify_greedy /
+    VerifyRound (the streaming regime: d % 128 == 0, B * (gamma + 1) <= 64)."""
+
+    def __init__(self, lm_head: torch.Tensor, stream=None):
+        _need(lm_head, "lm_head", torch.bfloat16)
+        V, d = lm_head.shape
+        nbytes = int(_lib.sd_lm_head_block_bytes(V, d))
+        if nbytes == 0:
+            raise ValueError(f"no blocked layout for a [{V}][{d}] LM head (d % 128 != 0)")
+        self.V, self.d, self.shape, self.nbytes = int(V), int(d), (int(V), int(d)), nbytes
+        self.buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=lm_head.device)
+        _check("sd_lm_head_block", _lib.sd_lm_head_block(_ptr(lm_head), V, d, _ptr(self.buf),
+                                                         nbytes, _stream(stream)))
+
+
 def _lm_head(lm_head, d):
-    """(pointer or descriptor, V, is_w12) of a bf16 LM head tensor or W12Weights."""
-    if isinstance(lm_head, W12Weights):
+    """(pointer or descriptor, V, entry-point suffix) of a bf16 LM head tensor,
+    W12Weights or BlockedWeights."""
+    if isinstance(lm_head, (W12Weights, BlockedWeights)):
         if lm_head.d != d:
             raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
-        return lm_head.descriptor(), lm_head.V, True
+        if isinstance(lm_head, W12Weights):
+            return lm_head.descriptor(), lm_head.V, "_w12"
+        return _ptr(lm_head.buf), lm_head.V, "_blocked"
     _need(lm_head, "lm_head", torch.bfloat16)
     if lm_head.shape[1] != d:
         raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
-    return _ptr(lm_head), lm_head.shape[0], False
+    return _ptr(lm_head), lm_head.shape[0], ""
 
 
 def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
@@ -318,11 +347,12 @@ def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
                      logits: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
     """Returns (logits or None, stats). Pass logits=True to have one allocated.
-    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_logits_w12 runs)."""
+    lm_head: bf16 [V][d] tensor, W12Weights (then sd_verify_logits_w12 runs) or
+    BlockedWeights (sd_verify_logits_blocked)."""
     _need(hidden, "hidden", torch.bfloat16)
     B, g1, d = hidden.shape
     g = g1 - 1
-    head, V, w12 = _lm_head(lm_head, d)
+    head, V, fmt = _lm_head(lm_head, d)
     dev = hidden.device
     if draft_tokens is not None:
         _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
@@ -339,7 +369,7 @@ def sd_verify_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
     _need(stats, "stats", torch.int64, (B * g1, 4))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
-    name = "sd_verify_logits_w12" if w12 else "sd_verify_logits"
+    name = "sd_verify_logits" + fmt
     _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(draft_tokens), _ptr(verify_len),
                                      _ptr(row_offsets), B, g, d, V, float(temperature),
                                      _ptr(logits), _ptr(stats), _ptr(workspace),
@@ -353,15 +383,16 @@ def sd_verify_contraction(hidden: torch.Tensor, lm_head: torch.Tensor,
                           logits: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None):
     """The contraction stage alone (logits and workspace partials, no row statistics).
-    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_contraction_w12 runs)."""
+    lm_head: bf16 [V][d] tensor, W12Weights (then sd_verify_contraction_w12 runs) or
+    BlockedWeights (sd_verify_contraction_blocked)."""
     _need(hidden, "hidden", torch.bfloat16)
     B, g1, d = hidden.shape
-    head, V, w12 = _lm_head(lm_head, d)
+    head, V, fmt = _lm_head(lm_head, d)
     if logits is not None:
         _need(logits, "logits", torch.float32, (B * g1, V))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g1 - 1, d, V), hidden.device, stream)
-    name = "sd_verify_contraction_w12" if w12 else "sd_verify_contraction"
+    name = "sd_verify_contraction" + fmt
     _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(verify_len), _ptr(row_offsets), B,
                                      g1 - 1, d, V, float(temperature), _ptr(logits),
                                      _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -377,11 +408,12 @@ def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: 
                      counters: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
     """Greedy verify in one call: returns (stats, accept_len, next_token).
-    lm_head: bf16 [V][d] tensor, or W12Weights (then sd_verify_greedy_w12 runs)."""
+    lm_head: bf16 [V][d] tensor, W12Weights (then sd_verify_greedy_w12 runs) or
+    BlockedWeights (sd_verify_greedy_blocked)."""
     _need(hidden, "hidden", torch.bfloat16)
     B, g1, d = hidden.shape
     g = g1 - 1
-    head, V, w12 = _lm_head(lm_head, d)
+    head, V, fmt = _lm_head(lm_head, d)
     dev = hidden.device
     _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
     if verify_len is not None:
@@ -398,7 +430,7 @@ def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: 
         _need(counters, "counters", torch.int64, (2,))
     if workspace is None:
         workspace = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
-    name = "sd_verify_greedy_w12" if w12 else "sd_verify_greedy"
+    name = "sd_verify_greedy" + fmt
     _check(name, getattr(_lib, name)(_ptr(hidden), head, _ptr(draft_tokens), _ptr(verify_len),
                                      _ptr(row_offsets), B, g, d, V, _ptr(stats), _ptr(accept_len),
                                      _ptr(next_token), _ptr(counters), _ptr(workspace),

@@ -128,7 +128,7 @@ namespace {
 
 // Shared validation and argument set-up of sd_verify_logits / sd_verify_contraction.
 int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
-                     const int32_t *draft_tokens, const int32_t *verify_len,
+                     bool blocked, const int32_t *draft_tokens, const int32_t *verify_len,
                      const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d, int32_t V,
                      float temperature, float *logits, sd_row_stats *stats, bool need_stats,
                      void *workspace, size_t workspace_bytes, VerifyArgs *out) {
@@ -142,6 +142,8 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
       return SD_ESHAPE;
     if (!aligned(w12->codes, 16) || !aligned(w12->corr, 16)) return SD_EALIGN;
   }
+  // The slab-blocked bf16 LM head, like W12, is read by the skinny contraction only.
+  if (blocked && (d % 128 != 0 || (int64_t)B * (gamma + 1) > 64)) return SD_ESHAPE;
   if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
   if (!isfinite(temperature) || temperature < 0.f) return SD_EINVAL;
   const int32_t sz = check_sizes(B, gamma, d, V);
@@ -159,6 +161,7 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
   VerifyArgs &a = *out;
   a.hidden = hidden;
   a.W = w12 ? nullptr : lm_head;
+  a.w_blocked = blocked;
   a.w12_codes = w12 ? w12->codes : nullptr;
   a.w12_corr = w12 ? w12->corr : nullptr;
   a.w12_cap = w12 ? w12->cap : 0;
@@ -189,17 +192,75 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
 
 }  // namespace
 
+}  // extern "C"
+
+namespace {
+
+// The three verify calls for any LM-head form: bf16 [V][d] (lm_head), W12 (w12) or the
+// slab-blocked bf16 copy (lm_head with blocked).
+int32_t verify_logits_impl(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
+                           bool blocked, const int32_t *draft_tokens, const int32_t *verify_len,
+                           const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                           int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, w12, blocked, draft_tokens, verify_len,
+                                  row_offsets, B, gamma, d, V, temperature, logits, stats, true,
+                                  workspace, workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  return launch_status(launch_verify(a, (hipStream_t)stream));
+}
+
+int32_t verify_contraction_impl(const uint16_t *hidden, const uint16_t *lm_head,
+                                const sd_w12 *w12, bool blocked, const int32_t *verify_len,
+                                const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                                int32_t V, float temperature, float *logits, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, w12, blocked, nullptr, verify_len, row_offsets,
+                                  B, gamma, d, V, temperature, logits, nullptr, false, workspace,
+                                  workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  int n_part = 0;
+  bool zx_done = false;
+  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part, &zx_done));
+}
+
+int32_t verify_greedy_impl(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
+                           bool blocked, const int32_t *draft_tokens, const int32_t *verify_len,
+                           const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                           int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                           int32_t *next_token, int64_t *counters, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (!draft_tokens || !accept_len || !next_token) return SD_EINVAL;
+  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
+    return SD_EALIGN;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, w12, blocked, draft_tokens, verify_len,
+                                  row_offsets, B, gamma, d, V, 0.f, nullptr, stats, true,
+                                  workspace, workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
+                                            (hipStream_t)stream));
+}
+
+// Bytes of the slab-blocked copy of a [V][d] LM head: ceil(V/64) * (d/128) blocks of 16 KB.
+size_t blocked_bytes(int32_t V, int32_t d) {
+  return (size_t)((V + 63) / 64) * (size_t)(d / 128) * 16384u;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t sd_verify_logits(const uint16_t *hidden, const uint16_t *lm_head,
                          const int32_t *draft_tokens, const int32_t *verify_len,
                          const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
                          int32_t V, float temperature, float *logits, sd_row_stats *stats,
                          void *workspace, size_t workspace_bytes, void *stream) {
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, nullptr, draft_tokens, verify_len, row_offsets,
-                                  B, gamma, d, V, temperature, logits, stats, true, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  return launch_status(launch_verify(a, (hipStream_t)stream));
+  return verify_logits_impl(hidden, lm_head, nullptr, false, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, temperature, logits, stats, workspace,
+                            workspace_bytes, stream);
 }
 
 int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
@@ -207,14 +268,9 @@ int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_head,
                               int32_t gamma, int32_t d, int32_t V, float temperature,
                               float *logits, void *workspace, size_t workspace_bytes,
                               void *stream) {
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, nullptr, nullptr, verify_len, row_offsets, B,
-                                  gamma, d, V, temperature, logits, nullptr, false, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  int n_part = 0;
-  bool zx_done = false;
-  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part, &zx_done));
+  return verify_contraction_impl(hidden, lm_head, nullptr, false, verify_len, row_offsets, B,
+                                 gamma, d, V, temperature, logits, workspace, workspace_bytes,
+                                 stream);
 }
 
 int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
@@ -223,16 +279,9 @@ int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
                          int32_t V, sd_row_stats *stats, int32_t *accept_len,
                          int32_t *next_token, int64_t *counters, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  if (!draft_tokens || !accept_len || !next_token) return SD_EINVAL;
-  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
-    return SD_EALIGN;
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, nullptr, draft_tokens, verify_len, row_offsets,
-                                  B, gamma, d, V, 0.f, nullptr, stats, true, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
-                                            (hipStream_t)stream));
+  return verify_greedy_impl(hidden, lm_head, nullptr, false, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, stats, accept_len, next_token, counters,
+                            workspace, workspace_bytes, stream);
 }
 
 int32_t sd_verify_logits_w12(const uint16_t *hidden, const sd_w12 *lm_head,
@@ -241,12 +290,9 @@ int32_t sd_verify_logits_w12(const uint16_t *hidden, const sd_w12 *lm_head,
                              int32_t V, float temperature, float *logits, sd_row_stats *stats,
                              void *workspace, size_t workspace_bytes, void *stream) {
   if (!lm_head) return SD_EINVAL;
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, nullptr, lm_head, draft_tokens, verify_len, row_offsets,
-                                  B, gamma, d, V, temperature, logits, stats, true, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  return launch_status(launch_verify(a, (hipStream_t)stream));
+  return verify_logits_impl(hidden, nullptr, lm_head, false, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, temperature, logits, stats, workspace,
+                            workspace_bytes, stream);
 }
 
 int32_t sd_verify_contraction_w12(const uint16_t *hidden, const sd_w12 *lm_head,
@@ -255,14 +301,9 @@ int32_t sd_verify_contraction_w12(const uint16_t *hidden, const sd_w12 *lm_head,
                                   float *logits, void *workspace, size_t workspace_bytes,
                                   void *stream) {
   if (!lm_head) return SD_EINVAL;
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, nullptr, lm_head, nullptr, verify_len, row_offsets, B,
-                                  gamma, d, V, temperature, logits, nullptr, false, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  int n_part = 0;
-  bool zx_done = false;
-  return launch_status(launch_contraction(a, (hipStream_t)stream, &n_part, &zx_done));
+  return verify_contraction_impl(hidden, nullptr, lm_head, false, verify_len, row_offsets, B,
+                                 gamma, d, V, temperature, logits, workspace, workspace_bytes,
+                                 stream);
 }
 
 int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_head,
@@ -271,16 +312,56 @@ int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_head,
                              int32_t V, sd_row_stats *stats, int32_t *accept_len,
                              int32_t *next_token, int64_t *counters, void *workspace,
                              size_t workspace_bytes, void *stream) {
-  if (!lm_head || !draft_tokens || !accept_len || !next_token) return SD_EINVAL;
-  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)))
-    return SD_EALIGN;
-  VerifyArgs a;
-  const int32_t st = verify_setup(hidden, nullptr, lm_head, draft_tokens, verify_len, row_offsets,
-                                  B, gamma, d, V, 0.f, nullptr, stats, true, workspace,
-                                  workspace_bytes, &a);
-  if (st != SD_OK) return st;
-  return launch_status(launch_verify_greedy(a, accept_len, next_token, counters,
-                                            (hipStream_t)stream));
+  if (!lm_head) return SD_EINVAL;
+  return verify_greedy_impl(hidden, nullptr, lm_head, false, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, stats, accept_len, next_token, counters,
+                            workspace, workspace_bytes, stream);
+}
+
+size_t sd_lm_head_block_bytes(int32_t V, int32_t d) {
+  if (V < 1 || d < 128 || d % 128 != 0) return 0;
+  return blocked_bytes(V, d);
+}
+
+int32_t sd_lm_head_block(const uint16_t *lm_head, int32_t V, int32_t d, uint16_t *blocked,
+                         size_t blocked_bytes_given, void *stream) {
+  if (!lm_head || !blocked) return SD_EINVAL;
+  if (V < 1 || d < 128 || d % 128 != 0) return SD_ESHAPE;
+  if (!aligned(lm_head, 16) || !aligned(blocked, 16)) return SD_EALIGN;
+  if (blocked_bytes_given < blocked_bytes(V, d)) return SD_EWORKSPACE;
+  return launch_status(launch_block_lm_head(lm_head, V, d, blocked, (hipStream_t)stream));
+}
+
+int32_t sd_verify_logits_blocked(const uint16_t *hidden, const uint16_t *lm_head_blocked,
+                                 const int32_t *draft_tokens, const int32_t *verify_len,
+                                 const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                                 int32_t V, float temperature, float *logits,
+                                 sd_row_stats *stats, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  return verify_logits_impl(hidden, lm_head_blocked, nullptr, true, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, temperature, logits, stats, workspace,
+                            workspace_bytes, stream);
+}
+
+int32_t sd_verify_contraction_blocked(const uint16_t *hidden, const uint16_t *lm_head_blocked,
+                                      const int32_t *verify_len, const int32_t *row_offsets,
+                                      int32_t B, int32_t gamma, int32_t d, int32_t V,
+                                      float temperature, float *logits, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  return verify_contraction_impl(hidden, lm_head_blocked, nullptr, true, verify_len, row_offsets,
+                                 B, gamma, d, V, temperature, logits, workspace, workspace_bytes,
+                                 stream);
+}
+
+int32_t sd_verify_greedy_blocked(const uint16_t *hidden, const uint16_t *lm_head_blocked,
+                                 const int32_t *draft_tokens, const int32_t *verify_len,
+                                 const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                                 int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                                 int32_t *next_token, int64_t *counters, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  return verify_greedy_impl(hidden, lm_head_blocked, nullptr, true, draft_tokens, verify_len,
+                            row_offsets, B, gamma, d, V, stats, accept_len, next_token, counters,
+                            workspace, workspace_bytes, stream);
 }
 
 int32_t sd_accept_greedy(const sd_row_stats *stats, const int32_t *draft_tokens,

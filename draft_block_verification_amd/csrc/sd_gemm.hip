@@ -314,6 +314,16 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
                                           int nt) {
   const int ng = a.d / 8;
   double part = 0.0;
+  if (a.w_blocked) {
+    // Block (x / 64, c / 16) holds row x & 63 at 128 values per row; chunk c & 15 sits at
+    // position (c & 15) ^ (x & 15).
+    const uint16_t *w = a.W + (size_t)(x >> 6) * (a.d / 128) * 8192 + (size_t)(x & 63) * 128;
+    for (int c = t; c < ng; c += nt)
+      part += dot8_f64(*reinterpret_cast<const u32x4 *>(h + 8 * c),
+                       *reinterpret_cast<const u32x4 *>(w + (size_t)(c >> 4) * 8192 +
+                                                        8 * ((c & 15) ^ (x & 15))));
+    return part;
+  }
   if (!a.w12_codes) {
     const uint16_t *w = a.W + (size_t)x * a.d;
     for (int c = t; c < ng; c += nt)
@@ -355,12 +365,13 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
 // bytes per row, stored in order) followed by the stage's correction slots; each
 // fragment is decoded right before its MFMA, and the lanes owning a corrected weight's
 // column add hidden * weight to their accumulators after the stage's MFMAs.
-template <int MT, int KC, int NS, bool W12>
+template <int MT, int KC, int NS, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) {
+  constexpr bool W12 = FMT == kLmW12, BLK = FMT == kLmBlocked;
   constexpr int BN = 64;
   constexpr int CH = KC / 8;                 // 16-byte chunks per bf16 stage row
   constexpr int RPI = 64 / CH;               // bf16 stage rows per wave instruction
-  static_assert((CH == 16 || CH == 32) && (!W12 || KC == 128), "stage shape");
+  static_assert((CH == 16 || CH == 32) && ((!W12 && !BLK) || KC == 128), "stage shape");
   // Stage layout in bytes: LM-head part, correction slots (W12), hidden rows.
   constexpr int WBYTES = W12 ? BN * KC * 3 / 2 : BN * KC * 2;
   constexpr int CBYTES = W12 ? 4 * kW12MaxCap : 0;
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   const uint16_t *h_src[HI];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    if (W12) {
+    if (W12 || BLK) {
       w_row[i] = 0;                           // the region is contiguous: piece u at 16 u
       w_off[i] = 16 * (64 * (wave + 4 * i) + lane);
     } else {
@@ -437,9 +448,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     LDSP char *dst = (LDSP char *)S + (size_t)(t % NS) * STAGE * 2;
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-      const GLBP char *src = W12
-          ? (const GLBP char *)(a.w12_codes + ((size_t)slab * nst + st) * WBYTES + w_off[i])
-          : (const GLBP char *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_off[i] + k0);
+      const GLBP char *src =
+          W12   ? (const GLBP char *)(a.w12_codes + ((size_t)slab * nst + st) * WBYTES + w_off[i])
+          : BLK ? (const GLBP char *)a.W + ((size_t)slab * nst + st) * WBYTES + w_off[i]
+                : (const GLBP char *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_off[i] + k0);
       __builtin_amdgcn_global_load_lds((const GLBP void *)src, (LDSP void *)(dst + (wave + 4 * i) * 1024),
                                        16, 0, kCachePolicyStream);
     }
@@ -1039,20 +1051,22 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
       else { t2 = fmaxf(t2, q[i].top1); }
     }
   }
-  // Without a logit from the contraction, the hidden and LM-head rows for the dot.
+  // Without a logit from the contraction, the hidden and LM-head rows for the dot (read
+  // here directly when the LM head is bf16 [V][d]).
   const bool need_dot = has_x && (!a.zx || zg != zg);
+  const bool rowmajor = !a.w12_codes && !a.w_blocked;
   u32x4 hv[kDotPer];
 #pragma unroll
   for (int i = 0; i < kDotPer; ++i) {
     const int c = tid + 256 * i;
-    hv[i] = need_dot && !a.w12_codes && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    hv[i] = need_dot && rowmajor && c < nc ? *reinterpret_cast<const u32x4 *>(hrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
-  const uint16_t *wrow = a.W ? a.W + (size_t)(has_x ? x : 0) * a.d : nullptr;
+  const uint16_t *wrow = rowmajor ? a.W + (size_t)(has_x ? x : 0) * a.d : nullptr;
   u32x4 wv[kDotPer];
 #pragma unroll
   for (int i = 0; i < kDotPer; ++i) {
     const int c = tid + 256 * i;
-    wv[i] = need_dot && !a.w12_codes && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    wv[i] = need_dot && rowmajor && c < nc ? *reinterpret_cast<const u32x4 *>(wrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
 
 #pragma unroll
@@ -1088,7 +1102,7 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   double zd = has_x ? zg : 0.0;
   if (need_dot) {
     double part = 0.0;
-    if (a.w12_codes) {
+    if (!rowmajor) {
       part = lm_head_dot_part(a, hrow, x, tid, 256);
     } else {
 #pragma unroll
@@ -1249,12 +1263,12 @@ int stage_stride(int nst) {
   return 1;
 }
 
-template <int MT, int KC, int NS, bool W12>
+template <int MT, int KC, int NS, int FMT>
 hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part) {
-  const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS, W12>);
+  const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS, FMT>);
   const int G = persistent_grid((a.V + 63) / 64, resident_blocks(fn), a.part_stride);
   *n_part = G;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, W12>), dim3(G), dim3(256), 0, stream, a,
+  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G), dim3(256), 0, stream, a,
                      stage_stride(a.d / KC));
   return hipGetLastError();
 }
@@ -1262,12 +1276,41 @@ hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part
 template <int MT, int KC, int NS>
 hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
   if constexpr (KC == 128) {
-    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, true>(a, stream, n_part);
+    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, kLmW12>(a, stream, n_part);
+    if (a.w_blocked) return launch_skinny_as<MT, KC, NS, kLmBlocked>(a, stream, n_part);
   }
-  return launch_skinny_as<MT, KC, NS, false>(a, stream, n_part);
+  return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part);
+}
+
+// Slab-blocked copy of a bf16 LM head: block (s, st) is 16 KB holding rows
+// 64 s .. 64 s + 63 and columns 128 st .. 128 st + 127, row r's 16-byte chunk j at
+// position j ^ (r & 15) -- the arrangement the streaming contraction keeps in LDS, so
+// one stage is one contiguous read -- and rows past V zero. One workgroup per block;
+// 16 lanes read one row's 256 bytes.
+__global__ __launch_bounds__(256) void k_block_lm_head(const uint16_t *__restrict__ W, int V,
+                                                       int d, uint16_t *__restrict__ out) {
+  const int nst = d / 128;
+  const size_t blk = blockIdx.x;
+  const int s = (int)(blk / nst), st = (int)(blk % nst);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int u = threadIdx.x + 256 * q;      // 16-byte piece of the block
+    const int r = u >> 4, j = (u & 15) ^ (r & 15);
+    const int v = 64 * s + r;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (v < V) val = *reinterpret_cast<const u32x4 *>(W + (size_t)v * d + 128 * st + 8 * j);
+    *reinterpret_cast<u32x4 *>(out + blk * 8192 + 8 * u) = val;
+  }
 }
 
 }  // namespace
+
+hipError_t launch_block_lm_head(const uint16_t *W, int V, int d, uint16_t *out,
+                                hipStream_t stream) {
+  const size_t blocks = (size_t)((V + 63) / 64) * (d / 128);
+  hipLaunchKernelGGL(k_block_lm_head, dim3((unsigned)blocks), dim3(256), 0, stream, W, V, d, out);
+  return hipGetLastError();
+}
 
 size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *part_stride,
                                size_t *zx_off) {

@@ -282,6 +282,51 @@ SD_API int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_hea
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Slab-blocked bf16 LM head: the same weights re-laid once so that the streaming
+ * contraction reads each of its stages (64 LM-head rows by 128 columns) as one
+ * contiguous 16 KB block. Layout: [ceil(V/64)][d/128][64][128] bf16; within a block,
+ * row r's 16-byte chunk j (columns 8j .. 8j + 7) sits at chunk position j ^ (r & 15);
+ * rows past V are zero. The values, and so every verify output, are those of the bf16
+ * [V][d] LM head. The LM head is static, so the copy is made once, beside the original.
+ *
+ * sd_lm_head_block_bytes: bytes of the copy (0 unless V >= 1 and d is a positive
+ * multiple of 128).
+ * sd_lm_head_block: writes the copy on `stream`.
+ *   lm_head  bf16 [V][d], 16-byte aligned; blocked: device buffer of
+ *   sd_lm_head_block_bytes(V, d) bytes, 16-byte aligned, not overlapping lm_head.
+ *   Errors: SD_EINVAL (null pointer), SD_ESHAPE (V < 1, d % 128 != 0), SD_EALIGN,
+ *   SD_EWORKSPACE (blocked_bytes too small), SD_EDEVICE.
+ * sd_verify_logits_blocked / sd_verify_contraction_blocked / sd_verify_greedy_blocked:
+ * sd_verify_logits / sd_verify_contraction / sd_verify_greedy reading the blocked copy
+ * (lm_head_blocked) instead of the [V][d] LM head; the streaming regime only, like W12:
+ * d % 128 == 0 and B * (gamma + 1) <= 64, else SD_ESHAPE. All other arguments, outputs
+ * and errors are those of the [V][d] calls.
+ */
+SD_API size_t sd_lm_head_block_bytes(int32_t V, int32_t d);
+SD_API int32_t sd_lm_head_block(const uint16_t *lm_head, int32_t V, int32_t d, uint16_t *blocked,
+                                size_t blocked_bytes, void *stream);
+SD_API int32_t sd_verify_logits_blocked(const uint16_t *hidden, const uint16_t *lm_head_blocked,
+                                        const int32_t *draft_tokens, const int32_t *verify_len,
+                                        const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                        int32_t d, int32_t V, float temperature, float *logits,
+                                        sd_row_stats *stats, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+SD_API int32_t sd_verify_contraction_blocked(const uint16_t *hidden,
+                                             const uint16_t *lm_head_blocked,
+                                             const int32_t *verify_len,
+                                             const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                             int32_t d, int32_t V, float temperature,
+                                             float *logits, void *workspace,
+                                             size_t workspace_bytes, void *stream);
+SD_API int32_t sd_verify_greedy_blocked(const uint16_t *hidden, const uint16_t *lm_head_blocked,
+                                        const int32_t *draft_tokens, const int32_t *verify_len,
+                                        const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                        int32_t d, int32_t V, sd_row_stats *stats,
+                                        int32_t *accept_len, int32_t *next_token,
+                                        int64_t *counters, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
  * Greedy acceptance (LFM2.5-DSpark blog, "Quality parity"): a_r = first j < L_r
  * with stats[row_offsets[r] + j].argmax != draft_tokens[r][j], else L_r; the
  * emitted token is the target argmax of row a_r (a correction when a_r < L_r,

@@ -152,6 +152,30 @@ def test_draft_normalizer_and_prenormalized_host_validation():
     assert r(*bad) == 4
 
 
+def test_lm_head_block_host_validation():
+    assert lib.sd_lm_head_block_bytes(1000, 256) == 16 * 2 * 16384
+    assert lib.sd_lm_head_block_bytes(64, 128) == 16384
+    assert lib.sd_lm_head_block_bytes(65, 128) == 2 * 16384
+    assert lib.sd_lm_head_block_bytes(100, 200) == 0          # d % 128 != 0
+    assert lib.sd_lm_head_block_bytes(0, 256) == 0
+    f = lib.sd_lm_head_block
+    ok = [FAKE, 1000, 256, FAKE, ctypes.c_size_t(16 * 2 * 16384), None]
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == 1
+    bad = list(ok); bad[2] = 200
+    assert f(*bad) == 2
+    bad = list(ok); bad[3] = ctypes.c_void_p(0x10008)
+    assert f(*bad) == 3
+    bad = list(ok); bad[4] = ctypes.c_size_t(16 * 2 * 16384 - 1)
+    assert f(*bad) == 4
+    v = lib.sd_verify_logits_blocked
+    args = [FAKE, FAKE, None, None, None, 8, 16, 256, 1000, ctypes.c_float(0.0), None, FAKE,
+            FAKE, ctypes.c_size_t(1 << 24), None]
+    assert v(*args) == 2                                       # 8 * 17 rows > 64
+    args[5], args[7] = 2, 200
+    assert v(*args) == 2                                       # d % 128 != 0
+
+
 def test_schedule_prefix_host_validation():
     f = lib.sd_schedule_prefix
 
