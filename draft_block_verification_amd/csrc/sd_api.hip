@@ -124,9 +124,11 @@ int32_t sd_schedule_prefix(const float *conf, const float *conf_stale, int32_t R
                                        row_offsets, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
 namespace {
 
-// Shared validation and argument set-up of sd_verify_logits / sd_verify_contraction.
+// Shared validation and argument set-up of the verify calls.
 int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
                      bool blocked, const int32_t *draft_tokens, const int32_t *verify_len,
                      const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d, int32_t V,
@@ -189,12 +191,6 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
   a.ws = reinterpret_cast<WsHeader *>(workspace);
   return SD_OK;
 }
-
-}  // namespace
-
-}  // extern "C"
-
-namespace {
 
 // The three verify calls for any LM-head form: bf16 [V][d] (lm_head), W12 (w12) or the
 // slab-blocked bf16 copy (lm_head with blocked).
