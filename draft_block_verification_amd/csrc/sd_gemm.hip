@@ -842,6 +842,9 @@ __global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a, int n_mt, int n
 // two waves per SIMD, which hides LDS read latency behind the other wave's MFMAs.
 // Rows of a stage are BK/8 16-byte chunks; chunk j of row r holds logical chunk
 // j ^ swz(r), so the MFMA fragment reads of 16 rows spread over the bank groups.
+// The LM-head fragment is the MFMA's first operand, so each lane ends with four
+// consecutive vocabulary ids of one row: 16-byte logits stores, and per-row
+// statistics that need two lane exchanges instead of four.
 template <int BM, int BN, int BK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, int n_nt) {
   constexpr int NT = 64 * NW;                      // threads
@@ -930,37 +933,45 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], af[i], acc[i][t], 0, 0, 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): the trailing reloads land before LDS is reused
   __syncthreads();
-  // Epilogue from registers, as in k_gemm_tile.
-  const int colb = v0 + wn * (BN / WNG) + fr;
+  // Epilogue from registers. With the LM-head fragment as the MFMA's first operand,
+  // lane (fr, fc) holds, for row tile i and vocabulary tile t, row
+  // wm * BM/2 + 16 i + fr at the four consecutive ids 16 t + 4 fc .. + 3.
+  const int vb = v0 + wn * (BN / WNG) + 4 * fc;
   if (a.logits) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * (BM / 2) + i * 16 + fr;
+      if (m < M) {
+        float *dst = a.logits + (size_t)m * V;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * (BM / 2) + i * 16 + 4 * fc + q;
-        if (m < M) {
-          float *dst = a.logits + (size_t)m * V;
+        for (int t = 0; t < TN; ++t) {
+          const int v = vb + t * 16;
+          if ((V & 3) == 0 && v + 4 <= V) {
+            *reinterpret_cast<f32x4 *>(dst + v) = acc[i][t];
+          } else {
 #pragma unroll
-          for (int t = 0; t < TN; ++t)
-            if (colb + t * 16 < V) dst[colb + t * 16] = acc[i][t][q];
+            for (int q = 0; q < 4; ++q)
+              if (v + q < V) dst[v + q] = acc[i][t][q];
+          }
         }
       }
+    }
   }
   float *X = reinterpret_cast<float *>(S);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    float t1 = -INFINITY, t2 = -INFINITY;
+    int a1 = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float t1 = -INFINITY, t2 = -INFINITY;
-      int a1 = 0x7fffffff;
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int v = colb + t * 16;
+      for (int q = 0; q < 4; ++q) {
+        const int v = vb + t * 16 + q;
         const float z = acc[i][t][q];
         if (v < V) {
           if (beats(z, v, t1, a1)) { t2 = t1; t1 = z; a1 = v; }
@@ -968,26 +979,28 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
         }
       }
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-        const int oa = __shfl_xor(a1, off);
-        if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-        else { t2 = fmaxf(t2, o1); }
-      }
-      float s = 0.f;
-      if (a.scale_log2 > 0.f) {
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-          if (colb + t * 16 < V) s += exp2f((acc[i][t][q] - t1) * a.scale_log2);
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      }
-      if (fr == 0) {
-        const int rl = wm * (BM / 2) + i * 16 + 4 * fc + q;
-        float *x = X + (wn * BM + rl) * 4;   // [WNG][BM][4]
-        x[0] = t1; x[1] = t2; x[2] = __int_as_float(a1); x[3] = s;
-      }
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+      const int oa = __shfl_xor(a1, off);
+      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+      else { t2 = fmaxf(t2, o1); }
     }
+    float s = 0.f;
+    if (a.scale_log2 > 0.f) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (vb + t * 16 + q < V) s += exp2f((acc[i][t][q] - t1) * a.scale_log2);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+    }
+    if (fc == 0) {
+      const int rl = wm * (BM / 2) + i * 16 + fr;
+      float *x = X + (wn * BM + rl) * 4;   // [WNG][BM][4]
+      x[0] = t1; x[1] = t2; x[2] = __int_as_float(a1); x[3] = s;
+    }
+  }
   __syncthreads();
   for (int rl = tid; rl < BM; rl += NT) {
     const int m = m0 + rl;
