@@ -143,6 +143,11 @@ struct RejArgs {
   WsHeader *ws;
 };
 
+// 2^x by the hardware instruction. It returns no denormals: results below 2^-126 are 0,
+// far below anything the sums and draws here resolve (each draw or sum is relative to a
+// row whose weights add up to 1).
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline double block_sum_d(double x, double *red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void k_draft_partial(RejArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
-      if (x[e] != -INFINITY) s += exp2f((x[e] - M) * a.sl);
+      if (x[e] != -INFINITY) s += exp2_hw((x[e] - M) * a.sl);
     const double S = block_sum_d((double)s, redd);
     if (threadIdx.x == 0) {
       DraftPart p;
@@ -293,10 +298,24 @@ __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
 }
 
 // The row being drawn from for request r: a_r after a rejection (residual), L_r otherwise.
+// A row's probabilities softmax(l / T)_v = exp(l_v / T - lse) formed in fp32 as
+// 2^((l_v - c) * sl) with c = lse * T and sl = log2(e) / T. For the ids that carry
+// weight l_v - c is small and nearly exact, and the rounding of c scales every weight
+// of the row by one common factor, which an inverse-CDF draw does not see.
+struct ProbScale {
+  float c, sl;
+};
+
+__device__ inline ProbScale prob_scale(double lse, const RejArgs &a) {
+  return ProbScale{(float)(lse / a.invT), a.sl};
+}
+
+__device__ inline float prob_of(float l, ProbScale s) { return exp2_hw((l - s.c) * s.sl); }
+
 struct DrawRow {
   const float *z;        // target logits of the row
   const uint16_t *q;     // drafter logits of the row (residual draws), else null
-  double lse_p, lse_q, invT;
+  ProbScale ps, qs;      // p and q of the row
 };
 
 __device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow) {
@@ -306,13 +325,12 @@ __device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow) 
   const int L = clamp_len(a.verify_len, r, gamma, nullptr);
   const int base = request_base(a.rm, r, L, nullptr);
   d->z = a.logits + (size_t)(base + acc) * a.V;
-  d->lse_p = a.stats[base + acc].lse;
-  d->invT = a.invT;
+  d->ps = prob_scale(a.stats[base + acc].lse, a);
   d->q = nullptr;
-  d->lse_q = 0.0;
+  d->qs = prob_scale(0.0, a);
   if (acc < L) {
     d->q = a.draft_logits + ((size_t)r * gamma + acc) * a.V;
-    d->lse_q = a.lse_q[(size_t)r * gamma + acc];
+    d->qs = prob_scale(a.lse_q[(size_t)r * gamma + acc], a);
   }
   *arow = base + acc;
   return true;
@@ -320,12 +338,9 @@ __device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow) 
 
 // p_v, and max(0, p_v - q_v) when the row has drafter logits.
 __device__ inline void draw_weights(const DrawRow &d, int v, float *p, float *res) {
-  *p = expf((float)((double)d.z[v] * d.invT - d.lse_p));
+  *p = prob_of(d.z[v], d.ps);
   *res = *p;
-  if (d.q) {
-    const float q = expf((float)((double)bf16_to_f32(d.q[v]) * d.invT - d.lse_q));
-    *res = fmaxf(*p - q, 0.f);
-  }
+  if (d.q) *res = fmaxf(*p - prob_of(bf16_to_f32(d.q[v]), d.qs), 0.f);
 }
 
 // ------------------------------------------------------ analytic acceptance rate
@@ -343,7 +358,7 @@ __device__ void rate_chunk(const RejArgs &a, int rj, int c, double *red) {
   if (base < 0) return;
   const float *z = a.logits + (size_t)(base + j) * a.V;
   const uint16_t *q = a.draft_logits + (size_t)rj * a.V;
-  const double lse_p = a.stats[base + j].lse, lse_q = a.lse_q[rj];
+  const ProbScale ps = prob_scale(a.stats[base + j].lse, a), qs = prob_scale(a.lse_q[rj], a);
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < kPer / 4; ++e) {
@@ -367,9 +382,7 @@ __device__ void rate_chunk(const RejArgs &a, int rj, int c, double *red) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (v0 + i < a.V) {
-        const float p = expf((float)((double)zf[i] * a.invT - lse_p));
-        const float qq = expf((float)((double)ql[i] * a.invT - lse_q));
-        s += (double)fminf(p, qq);
+        s += (double)fminf(prob_of(zf[i], ps), prob_of(ql[i], qs));
       }
     }
   }
@@ -429,9 +442,9 @@ __device__ void draw_chunk(const RejArgs &a, int r, int c, double *red) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (v0 + i < a.V) {
-        const float p = expf((float)((double)z[i] * d.invT - d.lse_p));
+        const float p = prob_of(z[i], d.ps);
         float w = p;
-        if (d.q) w = fmaxf(p - expf((float)((double)ql[i] * d.invT - d.lse_q)), 0.f);
+        if (d.q) w = fmaxf(p - prob_of(ql[i], d.qs), 0.f);
         sr += (double)w;
         sp += (double)p;
       }
@@ -546,7 +559,7 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
     for (int h = 0; h < kPer / 4; ++h) {
       const f32x4 zv = *reinterpret_cast<const f32x4 *>(d.z + v0 + 4 * h);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[4 * h + i] = expf((float)((double)zv[i] * d.invT - d.lse_p));
+      for (int i = 0; i < 4; ++i) w[4 * h + i] = prob_of(zv[i], d.ps);
     }
     if (d.q) {
 #pragma unroll
@@ -555,7 +568,7 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float ql = __uint_as_float((i & 1) ? (qv[i >> 1] & 0xffff0000u) : (qv[i >> 1] << 16));
-          w[8 * h + i] = fmaxf(w[8 * h + i] - expf((float)((double)ql * d.invT - d.lse_q)), 0.f);
+          w[8 * h + i] = fmaxf(w[8 * h + i] - prob_of(ql, d.qs), 0.f);
         }
       }
     }
