@@ -354,7 +354,10 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
 // stage buffers, so NS-1 stages stay in flight per workgroup with no registers held.
 // Wave w owns LM-head rows 16w..16w+15 of each 64-row slab over the full k range, so
 // a slab's 16 x 16 output tiles are complete in registers and its row statistics are
-// reduced with lane shuffles (no LDS round trip, no k-split reduction). A stage row
+// reduced with lane shuffles (no LDS round trip, no k-split reduction). The LM-head
+// fragment is the MFMA's first operand, so a lane ends a slab holding one hidden row at
+// four consecutive vocabulary ids: 16-byte logits stores, and two lane exchanges per
+// statistic. A stage row
 // holds KC/8 16-byte chunks; chunk j of row r holds logical chunk j ^ (r & 15).
 // LM-head loads carry the streaming (non-temporal) cache policy: every byte is used
 // once. Workgroup g walks the k stages of a slab starting at stage (g * kstride) mod
@@ -363,8 +366,8 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
 //
 // With W12 the LM-head part of a stage is the slab's 64 rows of 12-byte groups (192
 // bytes per row, stored in order) followed by the stage's correction slots; each
-// fragment is decoded right before its MFMA, and the lanes owning a corrected weight's
-// column add hidden * weight to their accumulators after the stage's MFMAs.
+// fragment is decoded right before its MFMA, and a corrected weight (coded as a signed
+// zero) gets its exact bits from the slot before the fragment enters the MFMA.
 template <int MT, int KC, int NS, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) {
   constexpr bool W12 = FMT == kLmW12, BLK = FMT == kLmBlocked;
@@ -471,11 +474,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   f32x4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  RowAcc run[MT][4];
+  RowAcc run[MT];                            // running statistics of row 16 i + fr
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) run[i][q] = row_acc_init();
+  for (int i = 0; i < MT; ++i) run[i] = row_acc_init();
   const int fr = lane & 15, fc = lane >> 4;
   const int br = 16 * wave + fr;
 
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
       for (int i = 0; i < MT; ++i) {
         const int hr = 16 * i + fr;
         const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Hb + hr * KC + 8 * (c ^ (hr & 15))));
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, av, acc[i], 0, 0, 0);
       }
     }
     if (t % nst == 0) {
@@ -569,34 +570,50 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
       }
     }
     if (t % nst == nst - 1) {
-      // Slab done. Lane l holds rows 16 i + 4 (l >> 4) + q, vocabulary id v; reduce
-      // over the 16 lanes that share l >> 4.
-      const int v = (g + (t / nst) * G) * BN + br;
-      const bool vok = v < V;
+      // Slab done. With the LM-head fragment as the MFMA's first operand, lane (fr, fc)
+      // holds row 16 i + fr at the four consecutive vocabulary ids vb .. vb + 3; reduce
+      // in registers, then over the four lanes that share fr.
+      const int vb = (g + (t / nst) * G) * BN + 16 * wave + 4 * fc;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        const int m = 16 * i + fr;
+        if (a.logits && m < M) {
+          float *dst = a.logits + (size_t)m * V;
+          if ((V & 3) == 0 && vb + 4 <= V) {
+            *reinterpret_cast<f32x4 *>(dst + vb) = acc[i];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (vb + q < V) dst[vb + q] = acc[i][q];
+          }
+        }
+        float t1 = -INFINITY, t2 = -INFINITY;
+        int a1 = 0x7fffffff;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float z = acc[i][q];
-          const int m = 16 * i + 4 * fc + q;
-          if (a.logits && vok && m < M) a.logits[(size_t)m * V + v] = z;
-          float t1 = vok ? z : -INFINITY, t2 = -INFINITY;
-          int a1 = vok ? v : 0x7fffffff;
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-            const int oa = __shfl_xor(a1, off);
-            if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-            else { t2 = fmaxf(t2, o1); }
+          if (vb + q < V) {
+            if (beats(z, vb + q, t1, a1)) { t2 = t1; t1 = z; a1 = vb + q; }
+            else if (z > t2) t2 = z;
           }
-          float s = 0.f;
-          if (a.scale_log2 > 0.f) {
-            s = vok ? exp2f((z - t1) * a.scale_log2) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
-          }
-          row_acc_merge(run[i][q], RowAcc{t1, t2, s, a1}, a.scale_log2);
         }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+          const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+          const int oa = __shfl_xor(a1, off);
+          if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+          else { t2 = fmaxf(t2, o1); }
+        }
+        float s = 0.f;
+        if (a.scale_log2 > 0.f) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (vb + q < V) s += exp2f((acc[i][q] - t1) * a.scale_log2);
+          s += __shfl_xor(s, 16);
+          s += __shfl_xor(s, 32);
+        }
+        row_acc_merge(run[i], RowAcc{t1, t2, s, a1}, a.scale_log2);
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (zrow >= 0) {
@@ -617,11 +634,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   // (row, workgroup). Every load into LDS has landed (the last pairs waited for all).
   __syncthreads();
   RowAcc *X = reinterpret_cast<RowAcc *>(S);   // [4][16 MT]
-  if (fr == 0) {
+  if (fc == 0) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) X[wave * 16 * MT + 16 * i + 4 * fc + q] = run[i][q];
+    for (int i = 0; i < MT; ++i) X[wave * 16 * MT + 16 * i + fr] = run[i];
   }
   __syncthreads();
   if (tid < 16 * MT && tid < M) {
