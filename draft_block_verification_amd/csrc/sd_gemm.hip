@@ -315,12 +315,13 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
   const int ng = a.d / 8;
   double part = 0.0;
   if (a.w_blocked) {
-    // Block (x / 64, c / 16) holds row x & 63 at 128 values per row; chunk c & 15 sits at
-    // position (c & 15) ^ (x & 15).
-    const uint16_t *w = a.W + (size_t)(x >> 6) * (a.d / 128) * 8192 + (size_t)(x & 63) * 128;
+    // Block (c / 16, x / 64) -- stage-major -- holds row x & 63 at 128 values per row;
+    // chunk c & 15 sits at position (c & 15) ^ (x & 15).
+    const size_t sstride = (size_t)((a.V + 63) / 64) * 8192;   // bf16 per stage of blocks
+    const uint16_t *w = a.W + (size_t)(x >> 6) * 8192 + (size_t)(x & 63) * 128;
     for (int c = t; c < ng; c += nt)
       part += dot8_f64(*reinterpret_cast<const u32x4 *>(h + 8 * c),
-                       *reinterpret_cast<const u32x4 *>(w + (size_t)(c >> 4) * 8192 +
+                       *reinterpret_cast<const u32x4 *>(w + (size_t)(c >> 4) * sstride +
                                                         8 * ((c & 15) ^ (x & 15))));
     return part;
   }
@@ -363,6 +364,8 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
 // once. Workgroup g walks the k stages of a slab starting at stage (g * kstride) mod
 // nst (kstride coprime to nst), so concurrent workgroups read different offsets of
 // their rows instead of all hitting the same column of power-of-two-strided rows.
+// The blocked bf16 layout is stage-major, so workgroups that walk their stages in step
+// (no offset) read one contiguous window of blocks at a time.
 //
 // With W12 the LM-head part of a stage is the slab's 64 rows of 12-byte groups (192
 // bytes per row, stored in order) followed by the stage's correction slots; each
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   const int nslab = (V + BN - 1) / BN;
   const int nst = d / KC;
   const int total = ((nslab - g + G - 1) / G) * nst;   // (slab, stage) pairs of this workgroup
-  const int kshift = (int)(((long long)g * kstride) % nst);
+  const int kshift = BLK ? 0 : (int)(((long long)g * kstride) % nst);
   const int cap = W12 ? a.w12_cap : 0;
   auto issue = [&](int t) {
     const int slab = g + (t / nst) * G, st = (t + kshift) % nst, k0 = st * KC;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     for (int i = 0; i < WI; ++i) {
       const GLBP char *src =
           W12   ? (const GLBP char *)(a.w12_codes + ((size_t)slab * nst + st) * WBYTES + w_off[i])
-          : BLK ? (const GLBP char *)a.W + ((size_t)slab * nst + st) * WBYTES + w_off[i]
+          : BLK ? (const GLBP char *)a.W + ((size_t)st * nslab + slab) * WBYTES + w_off[i]
                 : (const GLBP char *)(a.W + (size_t)min(slab * BN + w_row[i], V - 1) * d + w_off[i] + k0);
       __builtin_amdgcn_global_load_lds((const GLBP void *)src, (LDSP void *)(dst + (wave + 4 * i) * 1024),
                                        16, 0, kCachePolicyStream);
@@ -1310,16 +1313,17 @@ hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
   return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part);
 }
 
-// Slab-blocked copy of a bf16 LM head: block (s, st) is 16 KB holding rows
-// 64 s .. 64 s + 63 and columns 128 st .. 128 st + 127, row r's 16-byte chunk j at
-// position j ^ (r & 15) -- the arrangement the streaming contraction keeps in LDS, so
-// one stage is one contiguous read -- and rows past V zero. One workgroup per block;
-// 16 lanes read one row's 256 bytes.
+// Blocked copy of a bf16 LM head: block (st, s), stored stage-major at index
+// st * ceil(V/64) + s, is 16 KB holding rows 64 s .. 64 s + 63 and columns
+// 128 st .. 128 st + 127, row r's 16-byte chunk j at position j ^ (r & 15) -- the
+// arrangement the streaming contraction keeps in LDS, so one stage is one contiguous
+// read -- and rows past V zero. One workgroup per block; 16 lanes read one row's 256 bytes.
 __global__ __launch_bounds__(256) void k_block_lm_head(const uint16_t *__restrict__ W, int V,
                                                        int d, uint16_t *__restrict__ out) {
-  const int nst = d / 128;
+  const int nst = d / 128, nslab = (V + 63) / 64;
   const size_t blk = blockIdx.x;
   const int s = (int)(blk / nst), st = (int)(blk % nst);
+  uint16_t *dst = out + ((size_t)st * nslab + s) * 8192;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int u = threadIdx.x + 256 * q;      // 16-byte piece of the block
@@ -1327,7 +1331,7 @@ __global__ __launch_bounds__(256) void k_block_lm_head(const uint16_t *__restric
     const int v = 64 * s + r;
     u32x4 val = u32x4{0u, 0u, 0u, 0u};
     if (v < V) val = *reinterpret_cast<const u32x4 *>(W + (size_t)v * d + 128 * st + 8 * j);
-    *reinterpret_cast<u32x4 *>(out + blk * 8192 + 8 * u) = val;
+    *reinterpret_cast<u32x4 *>(dst + 8 * u) = val;
   }
 }
 

@@ -124,8 +124,8 @@ struct VerifyArgs {
   uint32_t w12_lut0, w12_lut1;
   sd_row_stats *stats;          // [cap]
   WsHeader *ws;
-  // Slab-blocked bf16 LM head: W holds [ceil(V/64)][d/128][64][128], row r's 16-byte
-  // chunk j of a block at position j ^ (r & 15), rows past V zero.
+  // Blocked bf16 LM head: W holds [d/128][ceil(V/64)][64][128] (stage-major), row r's
+  // 16-byte chunk j of a block at position j ^ (r & 15), rows past V zero.
   bool w_blocked;
 };
 

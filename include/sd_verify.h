@@ -284,9 +284,10 @@ SD_API int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_hea
 /*
  * Slab-blocked bf16 LM head: the same weights re-laid once so that the streaming
  * contraction reads each of its stages (64 LM-head rows by 128 columns) as one
- * contiguous 16 KB block. Layout: [ceil(V/64)][d/128][64][128] bf16; within a block,
- * row r's 16-byte chunk j (columns 8j .. 8j + 7) sits at chunk position j ^ (r & 15);
- * rows past V are zero. The values, and so every verify output, are those of the bf16
+ * contiguous 16 KB block. Layout: [d/128][ceil(V/64)][64][128] bf16, stage-major: block
+ * (st, s) holds LM-head rows 64 s .. 64 s + 63 at columns 128 st .. 128 st + 127, so the
+ * blocks of one column range are adjacent. Within a block, row r's 16-byte chunk j
+ * (columns 8j .. 8j + 7) sits at chunk position j ^ (r & 15); rows past V are zero. The values, and so every verify output, are those of the bf16
  * [V][d] LM head. The LM head is static, so the copy is made once, beside the original.
  *
  * sd_lm_head_block_bytes: bytes of the copy (0 unless V >= 1 and d is a positive

@@ -30,16 +30,20 @@ def need_gpu():
 
 
 def expected_blocks(W: np.ndarray) -> np.ndarray:
-    """The layout by its definition: [ceil(V/64)][d/128][64][128], row r's chunk j of a
-    block at chunk position j ^ (r & 15), rows past V zero."""
+    """The layout by its definition: [d/128][ceil(V/64)][64][128] (block (st, s) holds rows
+    64 s .. 64 s + 63 at columns 128 st .. 128 st + 127), row r's chunk j of a block at
+    chunk position j ^ (r & 15), rows past V zero."""
     V, d = W.shape
     ns, nst = (V + 63) // 64, d // 128
     pad = np.zeros((ns * 64, d), np.uint16)
     pad[:V] = W
-    out = np.zeros((ns, nst, 64, 16, 8), np.uint16)
-    for r in range(64):
-        for j in range(16):
-            out[:, :, r, j ^ (r & 15), :] = pad[r::64].reshape(ns, nst, 16, 8)[:, :, j, :]
+    out = np.zeros((nst, ns, 64, 16, 8), np.uint16)
+    for st in range(nst):
+        for s in range(ns):
+            for r in range(64):
+                row = pad[64 * s + r, 128 * st:128 * (st + 1)].reshape(16, 8)
+                for j in range(16):
+                    out[st, s, r, j ^ (r & 15), :] = row[j]
     return out.reshape(-1)
 
 
