@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void k_accept_greedy(const sd_row_stats *__res
 // Four wide kernels, each over chunks of kChunk vocabulary ids (grid x = chunk,
 // grid y strides over rows or requests, so that concurrent workgroups stream
 // neighbouring chunks of one row):
-//   k_draft_partial   (chunk, draft row): max and sum of exp((l - max) / T) of the
-//                     drafter logits, for every kept draft row;
+//   k_draft_partial   (chunk, draft row), one wave each: max and sum of
+//                     exp((l - max) / T) of the drafter logits, for every kept draft row;
 //   k_accept_decide   (request): merge those into log q-normalisers, then accept
 //                     draft j iff u_accept < min(1, p_j(x_j) / q_j(x_j)) and take the
 //                     first rejection a_r (or L_r);
@@ -159,60 +159,84 @@ __device__ inline double block_sum_d(double x, double *red) {
   return r;
 }
 
-__device__ inline float block_max_f(float x, float *red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
+// One wave per (chunk, kept draft row): the chunk's 4096 drafter logits arrive as eight
+// 1 KB wave loads (load h gives lane l ids c * kChunk + 512 h + 8 l .. + 7; ids past V
+// count as -inf), and the chunk's max and sum are reduced with lane exchanges only, with
+// no workgroup barrier. A workgroup's waves take neighbouring chunks of one row; grid y
+// strides over the rows. Rows are 16-byte aligned when V % 8 == 0; otherwise the chunk
+// is read one id at a time (two passes).
+constexpr int kDraftWaves = 4;
 
-// kPer drafter logits of chunk c held by this thread: ids c*kChunk + 8*(tid + 256 h) + e
-// for h < kPer/8, e < 8 (each wave load is 1 KB contiguous); -inf past V.
-__device__ inline void load_draft_chunk(const uint16_t *row, int V, int c, float *x) {
-#pragma unroll
-  for (int h = 0; h < kPer / 8; ++h) {
-    const int v0 = c * kChunk + 8 * (threadIdx.x + 256 * h);
-    if ((V & 7) == 0 && v0 + 8 <= V) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[8 * h + 2 * q] = __uint_as_float(w[q] << 16);
-        x[8 * h + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * h + e] = v0 + e < V ? bf16_to_f32(row[v0 + e]) : -INFINITY;
-    }
-  }
-}
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__global__ __launch_bounds__(256) void k_draft_partial(RejArgs a) {
-  __shared__ float redf[4];
-  __shared__ double redd[4];
-  const int gamma = a.rm.gamma, c = blockIdx.x;
+__global__ __launch_bounds__(64 * kDraftWaves) void k_draft_partial(RejArgs a) {
+  const int gamma = a.rm.gamma, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * kDraftWaves + (threadIdx.x >> 6);
+  if (c >= a.C) return;
+  const int V = a.V;
+  const bool aligned = (V & 7) == 0;
   for (int rj = blockIdx.y; rj < a.rm.B * gamma; rj += gridDim.y) {
     const int r = rj / gamma, j = rj - r * gamma;
-    const int L = clamp_len(a.verify_len, r, gamma, threadIdx.x == 0 ? a.ws : nullptr);
+    const int L = clamp_len(a.verify_len, r, gamma, c == 0 && lane == 0 ? a.ws : nullptr);
     if (j >= L) continue;
-    const uint16_t *row = a.draft_logits + (size_t)rj * a.V;
-    float x[kPer];
-    load_draft_chunk(row, a.V, c, x);
-    float cm = x[0];
+    const uint16_t *row = a.draft_logits + (size_t)rj * V;
+    float m = -INFINITY;
+    float sh[8];
+    if (aligned) {
+      u32x4 w[8];
 #pragma unroll
-    for (int e = 1; e < kPer; ++e) cm = fmaxf(cm, x[e]);
-    const float M = block_max_f(cm, redf);
-    float s = 0.f;
+      for (int h = 0; h < 8; ++h) {
+        const int v0 = c * kChunk + 512 * h + 8 * lane;   // v0 < V implies v0 + 8 <= V
+        w[h] = v0 < V ? *reinterpret_cast<const u32x4 *>(row + v0)
+                      : u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // bf16 -inf
+      }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (x[e] != -INFINITY) s += exp2_hw((x[e] - M) * a.sl);
-    const double S = block_sum_d((double)s, redd);
-    if (threadIdx.x == 0) {
+      for (int h = 0; h < 8; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(bf_lo(w[h][q]), bf_hi(w[h][q])));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        sh[h] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sh[h] += exp2_hw((bf_lo(w[h][q]) - m) * a.sl);
+          sh[h] += exp2_hw((bf_hi(w[h][q]) - m) * a.sl);
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int h = 0; h < 8; ++h)
+#pragma unroll 1
+        for (int e = 0; e < 8; ++e) {
+          const int v = c * kChunk + 512 * h + 8 * lane + e;
+          if (v < V) m = fmaxf(m, bf16_to_f32(row[v]));
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        sh[h] = 0.f;
+#pragma unroll 1
+        for (int e = 0; e < 8; ++e) {
+          const int v = c * kChunk + 512 * h + 8 * lane + e;
+          if (v < V) sh[h] += exp2_hw((bf16_to_f32(row[v]) - m) * a.sl);
+        }
+      }
+    }
+    // Ids at -inf add exp2(-inf) = 0; a chunk that is -inf throughout sums to 0.
+    double S = 0.0;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int h = 0; h < 8; ++h) S += (double)sh[h];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    }
+    if (lane == 0) {
       DraftPart p;
-      p.m = M; p.pad = 0.f; p.s = S;
+      p.m = m; p.pad = 0.f; p.s = S;
       a.dpart[(size_t)rj * a.C + c] = p;
     }
   }
@@ -683,7 +707,8 @@ hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *
                                    hipStream_t stream) {
   const RowMap rm{nullptr, B, gamma};
   const RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
-  hipLaunchKernelGGL(k_draft_partial, dim3(a.C, grid_rows(B * gamma)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_draft_partial, dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(B * gamma)),
+                     dim3(64 * kDraftWaves), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -709,8 +734,9 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
   a.rate = accept_rate;
   hipError_t e;
   if (!normalized) {
-    hipLaunchKernelGGL(k_draft_partial, dim3(a.C, grid_rows(rm.B * rm.gamma)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL(k_draft_partial,
+                       dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(rm.B * rm.gamma)),
+                       dim3(64 * kDraftWaves), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
