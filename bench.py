@@ -64,8 +64,10 @@ def parse():
                          "regime only")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="T > 0: run the drafter-row normaliser on a second stream beside the "
-                         "contraction (sd_draft_normalizer + sd_accept_rejection_prenormalized); "
-                         "measured 0.6-5%% slower on the rejection workloads, so off by default")
+                         "contraction (sd_draft_normalizer + sd_accept_rejection_prenormalized)")
+    ap.add_argument("--overlap-workgroups", type=int, default=None,
+                    help="with --overlap on: workgroups of the side-stream normaliser "
+                         "(default: one per 32 compute units)")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the verify benchmark: the toy multi-step decode loop "
                          "(bigram target over the workload's LM head, drafter table right 75%% "
@@ -189,7 +191,7 @@ def main():
         sps = sd.profile_sps(w.B, w.gamma, W_dev[0], w.T)
     vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold, device=dev,
                         accept_rate=args.accept_rate, scheduler=sched, sps=sps,
-                        overlap=args.overlap == "on")
+                        overlap=args.overlap == "on", overlap_workgroups=args.overlap_workgroups)
     stream = torch.cuda.Stream(device=dev)
 
     # The threshold reads survival confidences; the scheduler reads the conditional ones
@@ -348,7 +350,7 @@ def main():
                    "lm_head_copies": n_copies, "mean_rows": mean_rows,
                    "launch": "eager" if args.eager else "hipgraph",
                    "accept_rate": vr.accept_rate is not None,
-                   "overlap": vr.side is not None,
+                   "overlap": vr.overlap_workgroups if vr.side is not None else False,
                    "scheduler": args.scheduler,
                    "lm_head_format": args.weights,
                    # Expected tokens per second if the confidences are calibrated survival

@@ -60,7 +60,7 @@ _SIGS = {
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_accept_rejection_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "sd_draft_normalizer": (_i32, [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "sd_draft_normalizer": (_i32, [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _sz, _i32, _vp]),
     "sd_accept_rejection_prenormalized": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                  _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz,
                                                  _vp]),
@@ -495,9 +495,11 @@ def sd_accept_rejection_ex(logits: torch.Tensor, stats: torch.Tensor, draft_logi
 
 
 def sd_draft_normalizer(draft_logits: torch.Tensor, verify_len: Optional[torch.Tensor],
-                        temperature: float, workspace: torch.Tensor, stream=None) -> None:
+                        temperature: float, workspace: torch.Tensor, stream=None,
+                        workgroups: int = 0) -> None:
     """Drafter-row normaliser alone, into the accept workspace (see
-    sd_accept_rejection_prenormalized); independent of the verify outputs."""
+    sd_accept_rejection_prenormalized); independent of the verify outputs. workgroups > 0
+    runs that fixed number of workgroups (a bounded footprint beside the contraction)."""
     _need(draft_logits, "draft_logits", torch.bfloat16)
     B, g, V = draft_logits.shape
     if verify_len is not None:
@@ -506,7 +508,7 @@ def sd_draft_normalizer(draft_logits: torch.Tensor, verify_len: Optional[torch.T
     _check("sd_draft_normalizer",
            _lib.sd_draft_normalizer(_ptr(draft_logits), _ptr(verify_len), B, g, V,
                                     float(temperature), _ptr(workspace), workspace.numel(),
-                                    _stream(stream)))
+                                    int(workgroups), _stream(stream)))
 
 
 def sd_accept_rejection_prenormalized(logits: torch.Tensor, stats: torch.Tensor,
@@ -574,13 +576,16 @@ class VerifyRound:
     the separate sd_verify_logits + sd_accept_greedy calls. With overlap=True (T > 0)
     the drafter-row normaliser runs on a second stream beside sd_verify_logits (it
     needs only the kept lengths), joined before sd_accept_rejection_prenormalized; the
-    fork and join are stream waits, so the round still captures into one graph.
+    fork and join are stream waits, so the round still captures into one graph. There
+    it runs as a fixed grid of overlap_workgroups 16-wave workgroups (default: one per
+    32 compute units, i.e. one per XCD), which bounds the compute units it holds.
     """
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
                  truncate: bool, threshold: float = 0.3, device="cuda", stream=None,
                  fused: bool = True, accept_rate: bool = False, scheduler: Optional[int] = None,
-                 sps: Optional[torch.Tensor] = None, overlap: bool = False):
+                 sps: Optional[torch.Tensor] = None, overlap: bool = False,
+                 overlap_workgroups: Optional[int] = None):
         self.B, self.gamma, self.d, self.V = B, gamma, d, V
         # With a scheduler mode (SCHED_EARLY_STOP / SCHED_TOP_K) and an SPS table, the
         # prefix scheduler replaces the confidence threshold.
@@ -606,6 +611,10 @@ class VerifyRound:
         self.accept_rate = (torch.empty((B, gamma), dtype=torch.float64, device=dev)
                             if accept_rate and self.T > 0 else None)
         self.side = torch.cuda.Stream(device=dev) if overlap and self.T > 0 else None
+        if overlap_workgroups is None:
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count if self.side else 8
+            overlap_workgroups = max(1, cus // 32)
+        self.overlap_workgroups = int(overlap_workgroups)
 
     def run(self, hidden, lm_head, draft_tokens, conf=None, draft_logits=None, u_accept=None,
             u_resample=None, stream=None, conf_stale=None):
@@ -625,7 +634,7 @@ class VerifyRound:
             main = stream if stream is not None else torch.cuda.current_stream()
             self.side.wait_stream(main)                       # kept lengths are ready
             sd_draft_normalizer(draft_logits, self.verify_len, self.T, self.ws_accept,
-                                stream=self.side)
+                                stream=self.side, workgroups=self.overlap_workgroups)
             sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                              self.T, self.logits, self.stats, self.ws_verify, stream=main)
             main.wait_stream(self.side)

@@ -159,86 +159,169 @@ __device__ inline double block_sum_d(double x, double *red) {
   return r;
 }
 
-// One wave per (chunk, kept draft row): the chunk's 4096 drafter logits arrive as eight
-// 1 KB wave loads (load h gives lane l ids c * kChunk + 512 h + 8 l .. + 7; ids past V
-// count as -inf), and the chunk's max and sum are reduced with lane exchanges only, with
-// no workgroup barrier. A workgroup's waves take neighbouring chunks of one row; grid y
-// strides over the rows. Rows are 16-byte aligned when V % 8 == 0; otherwise the chunk
-// is read one id at a time (two passes).
+// Drafter-row normaliser, one wave per (chunk, kept draft row): the chunk's 4096 drafter
+// logits arrive as eight 1 KB wave loads (load h gives lane l ids c * kChunk + 512 h + 8 l
+// .. + 7; ids past V count as -inf), and the chunk's max and sum are reduced with lane
+// exchanges only, with no workgroup barrier. Rows are 16-byte aligned when V % 8 == 0;
+// otherwise the chunk is read one id at a time (two passes).
 constexpr int kDraftWaves = 4;
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Loads of chunk c of an aligned row (V % 8 == 0, so V >= 8 and v0 < V means v0 + 8 <= V).
+// The address is clamped into the row, so every lane loads; past V the value is -inf.
+__device__ inline void draft_chunk_load(const uint16_t *row, int V, int c, int lane, u32x4 (&w)[8]) {
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const int v0 = c * kChunk + 512 * h + 8 * lane;
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + min(v0, V - 8)));
+    const u32x4 ninf{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // bf16 -inf
+    w[h] = v0 < V ? x : ninf;
+  }
+}
+
+// Ids at -inf add exp2(-inf) = 0; a chunk that is -inf throughout sums to 0.
+__device__ inline DraftPart draft_part(float m, const float (&sh)[8]) {
+  double S = 0.0;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) S += (double)sh[h];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  }
+  DraftPart p;
+  p.m = m; p.pad = 0.f; p.s = S;
+  return p;
+}
+
+__device__ inline DraftPart draft_chunk_stats(const u32x4 (&w)[8], float sl) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(bf_lo(w[h][q]), bf_hi(w[h][q])));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float sh[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    sh[h] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sh[h] += exp2_hw((bf_lo(w[h][q]) - m) * sl);
+      sh[h] += exp2_hw((bf_hi(w[h][q]) - m) * sl);
+    }
+  }
+  return draft_part(m, sh);
+}
+
+__device__ inline DraftPart draft_chunk_unaligned(const uint16_t *row, int V, int c, int lane,
+                                                  float sl) {
+  float m = -INFINITY;
+#pragma unroll 1
+  for (int h = 0; h < 8; ++h)
+#pragma unroll 1
+    for (int e = 0; e < 8; ++e) {
+      const int v = c * kChunk + 512 * h + 8 * lane + e;
+      if (v < V) m = fmaxf(m, bf16_to_f32(row[v]));
+    }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float sh[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    sh[h] = 0.f;
+#pragma unroll 1
+    for (int e = 0; e < 8; ++e) {
+      const int v = c * kChunk + 512 * h + 8 * lane + e;
+      if (v < V) sh[h] += exp2_hw((bf16_to_f32(row[v]) - m) * sl);
+    }
+  }
+  return draft_part(m, sh);
+}
+
+// Full grid: a workgroup's waves take neighbouring chunks of one row; grid y strides over
+// the rows.
 __global__ __launch_bounds__(64 * kDraftWaves) void k_draft_partial(RejArgs a) {
   const int gamma = a.rm.gamma, lane = threadIdx.x & 63;
   const int c = blockIdx.x * kDraftWaves + (threadIdx.x >> 6);
   if (c >= a.C) return;
   const int V = a.V;
-  const bool aligned = (V & 7) == 0;
   for (int rj = blockIdx.y; rj < a.rm.B * gamma; rj += gridDim.y) {
     const int r = rj / gamma, j = rj - r * gamma;
     const int L = clamp_len(a.verify_len, r, gamma, c == 0 && lane == 0 ? a.ws : nullptr);
     if (j >= L) continue;
     const uint16_t *row = a.draft_logits + (size_t)rj * V;
-    float m = -INFINITY;
-    float sh[8];
-    if (aligned) {
+    DraftPart p;
+    if ((V & 7) == 0) {
       u32x4 w[8];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        const int v0 = c * kChunk + 512 * h + 8 * lane;   // v0 < V implies v0 + 8 <= V
-        w[h] = v0 < V ? *reinterpret_cast<const u32x4 *>(row + v0)
-                      : u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // bf16 -inf
-      }
-#pragma unroll
-      for (int h = 0; h < 8; ++h)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(bf_lo(w[h][q]), bf_hi(w[h][q])));
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-#pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        sh[h] = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sh[h] += exp2_hw((bf_lo(w[h][q]) - m) * a.sl);
-          sh[h] += exp2_hw((bf_hi(w[h][q]) - m) * a.sl);
-        }
-      }
+      draft_chunk_load(row, V, c, lane, w);
+      p = draft_chunk_stats(w, a.sl);
     } else {
-#pragma unroll 1
-      for (int h = 0; h < 8; ++h)
-#pragma unroll 1
-        for (int e = 0; e < 8; ++e) {
-          const int v = c * kChunk + 512 * h + 8 * lane + e;
-          if (v < V) m = fmaxf(m, bf16_to_f32(row[v]));
-        }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-#pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        sh[h] = 0.f;
-#pragma unroll 1
-        for (int e = 0; e < 8; ++e) {
-          const int v = c * kChunk + 512 * h + 8 * lane + e;
-          if (v < V) sh[h] += exp2_hw((bf16_to_f32(row[v]) - m) * a.sl);
-        }
+      p = draft_chunk_unaligned(row, V, c, lane, a.sl);
+    }
+    if (lane == 0) a.dpart[(size_t)rj * a.C + c] = p;
+  }
+}
+
+// Bounded footprint, for running beside the contraction on another stream: a fixed grid
+// of 16-wave workgroups whose waves walk the (draft row, chunk) items in row-major order
+// with a stride of the grid's wave count, skipping rows past L_r, with the next item's
+// loads in flight while the current one is reduced. Many waves per workgroup keep the
+// work on few compute units (workgroups reach the XCDs in turn, so a grid of one per XCD
+// holds one compute unit on each). Same partials, bit for bit, as k_draft_partial.
+constexpr int kWalkWaves = 16;
+
+__global__ __launch_bounds__(64 * kWalkWaves) void k_draft_partial_walk(RejArgs a) {
+  const int gamma = a.rm.gamma, C = a.C, V = a.V, lane = threadIdx.x & 63;
+  const int rows = a.rm.B * gamma;
+  // The walk state is wave-uniform; readfirstlane keeps it in scalar registers, so the
+  // kept-length lookups are scalar loads that do not wait on the vector loads in flight.
+  const int nw = gridDim.x * kWalkWaves;
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWalkWaves + (threadIdx.x >> 6));
+  const int dq = nw / C, dr = nw % C;
+  int rj = gw / C, c = gw % C;
+  int r_seen = -1, L_seen = 0;      // kept length of the last request looked up
+  auto step = [&]() {
+    rj += dq;
+    c += dr;
+    if (c >= C) { c -= C; ++rj; }
+  };
+  auto seek = [&]() {        // advance (rj, c) to the first item of a kept row, or rj >= rows
+    while (rj < rows) {
+      const int r = rj / gamma;
+      if (r != r_seen) {
+        r_seen = r;
+        L_seen = clamp_len(a.verify_len, r, gamma, lane == 0 ? a.ws : nullptr);
       }
+      if (rj - r * gamma < L_seen) return;
+      step();
     }
-    // Ids at -inf add exp2(-inf) = 0; a chunk that is -inf throughout sums to 0.
-    double S = 0.0;
-    if (m != -INFINITY) {
+  };
+  seek();
+  if ((V & 7) != 0) {
+    for (; rj < rows; step(), seek()) {
+      const DraftPart p = draft_chunk_unaligned(a.draft_logits + (size_t)rj * V, V, c, lane, a.sl);
+      if (lane == 0) a.dpart[(size_t)rj * C + c] = p;
+    }
+    return;
+  }
+  u32x4 w[8];
+  if (rj < rows) draft_chunk_load(a.draft_logits + (size_t)rj * V, V, c, lane, w);
+  while (rj < rows) {
+    const int cur_rj = rj, cur_c = c;
+    step();
+    seek();
+    // Next item's loads (past the end: the current item again, never used), issued on
+    // every path so the wait before the reduction below leaves them in flight.
+    const int nrj = rj < rows ? rj : cur_rj, nc = rj < rows ? c : cur_c;
+    u32x4 wn[8];
+    draft_chunk_load(a.draft_logits + (size_t)nrj * V, V, nc, lane, wn);
+    const DraftPart p = draft_chunk_stats(w, a.sl);
+    if (lane == 0) a.dpart[(size_t)cur_rj * C + cur_c] = p;
 #pragma unroll
-      for (int h = 0; h < 8; ++h) S += (double)sh[h];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-    }
-    if (lane == 0) {
-      DraftPart p;
-      p.m = m; p.pad = 0.f; p.s = S;
-      a.dpart[(size_t)rj * a.C + c] = p;
-    }
+    for (int h = 0; h < 8; ++h) w[h] = wn[h];
   }
 }
 
@@ -704,11 +787,14 @@ RejArgs rej_args(const uint16_t *draft_logits, const int32_t *verify_len, const 
 
 hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
                                    int B, int gamma, int V, float temperature, void *workspace,
-                                   hipStream_t stream) {
+                                   int workgroups, hipStream_t stream) {
   const RowMap rm{nullptr, B, gamma};
   const RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
-  hipLaunchKernelGGL(k_draft_partial, dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(B * gamma)),
-                     dim3(64 * kDraftWaves), 0, stream, a);
+  if (workgroups > 0)
+    hipLaunchKernelGGL(k_draft_partial_walk, dim3(workgroups), dim3(64 * kWalkWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_draft_partial, dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(B * gamma)),
+                       dim3(64 * kDraftWaves), 0, stream, a);
   return hipGetLastError();
 }
 

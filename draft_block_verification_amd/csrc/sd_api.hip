@@ -419,15 +419,16 @@ int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
 
 int32_t sd_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len, int32_t B,
                             int32_t gamma, int32_t V, float temperature, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            size_t workspace_bytes, int32_t workgroups, void *stream) {
   if (!draft_logits) return SD_EINVAL;
+  if (workgroups < 0 || workgroups > 65535) return SD_EINVAL;
   if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
   if (check_sizes(B, gamma, 8, V) != SD_OK) return SD_ESHAPE;
   if (!aligned(draft_logits, 16) || (verify_len && !aligned(verify_len, 4))) return SD_EALIGN;
   if (!workspace || workspace_bytes < accept_ws_bytes(B, gamma, V)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
   return launch_status(launch_draft_normalizer(draft_logits, verify_len, B, gamma, V, temperature,
-                                               workspace, (hipStream_t)stream));
+                                               workspace, workgroups, (hipStream_t)stream));
 }
 
 int32_t sd_accept_rejection_prenormalized(

@@ -57,8 +57,10 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
                                    float temperature, int32_t *accept_len, int32_t *next_token,
                                    int64_t *counters, double *accept_rate, void *workspace,
                                    bool normalized, hipStream_t stream);
+// workgroups > 0: a fixed grid of that many workgroups walking the rows (bounded
+// footprint beside another kernel); 0: one wave per (chunk, kept row) over a full grid.
 hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
                                    int B, int gamma, int V, float temperature, void *workspace,
-                                   hipStream_t stream);
+                                   int workgroups, hipStream_t stream);
 
 }  // namespace sdv

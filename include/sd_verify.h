@@ -407,12 +407,21 @@ SD_API int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *s
  *   temperature  > 0, the one the acceptance call will get
  *   workspace    the accept workspace (sd_accept_workspace_bytes(B, gamma, V) bytes,
  *                256-byte aligned); this call writes its drafter chunk partials
- * Errors: SD_EINVAL (null drafter logits, temperature not finite and positive),
- * SD_ESHAPE, SD_EALIGN, SD_EWORKSPACE, SD_EDEVICE. Rows j >= L_r are not read.
+ *   workgroups   0: one wave per (4096-id chunk, kept row) over a grid as large as the
+ *                rows need, the fastest form on an idle GPU; 1 .. 65535: exactly that
+ *                many workgroups of 1024 threads, whose waves walk the (row, chunk) items
+ *                in turn. The second form bounds how much of the GPU the call holds, so
+ *                that beside sd_verify_logits on another stream it fills compute units
+ *                the contraction leaves idle instead of delaying it. The partials are the
+ *                same bytes either way.
+ * Errors: SD_EINVAL (null drafter logits, temperature not finite and positive,
+ * workgroups outside [0, 65535]), SD_ESHAPE, SD_EALIGN, SD_EWORKSPACE, SD_EDEVICE.
+ * Rows j >= L_r are not read.
  */
 SD_API int32_t sd_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
                                    int32_t B, int32_t gamma, int32_t V, float temperature,
-                                   void *workspace, size_t workspace_bytes, void *stream);
+                                   void *workspace, size_t workspace_bytes, int32_t workgroups,
+                                   void *stream);
 
 /*
  * sd_accept_rejection_ex without its drafter-row normaliser: the workspace must hold

@@ -122,10 +122,14 @@ def test_accept_rejection_ex_host_validation():
 
 def test_draft_normalizer_and_prenormalized_host_validation():
     n = lib.sd_draft_normalizer
-    args = [FAKE, None, 1, 4, 1024, ctypes.c_float(1.0), FAKE, ctypes.c_size_t(1 << 20), None]
+    args = [FAKE, None, 1, 4, 1024, ctypes.c_float(1.0), FAKE, ctypes.c_size_t(1 << 20), 0, None]
     bad = list(args)
     bad[0] = None
     assert n(*bad) == 1                               # drafter logits required
+    for wg in (-1, 65536):
+        bad = list(args)
+        bad[8] = wg
+        assert n(*bad) == 1                           # workgroups outside [0, 65535]
     bad = list(args)
     bad[5] = ctypes.c_float(float("nan"))
     assert n(*bad) == 1

@@ -436,3 +436,38 @@ def test_overlapped_normalizer_matches_single_stream(case):
         if rate:
             assert (ref.accept_rate.cpu().numpy().tobytes() ==
                     ovl.accept_rate.cpu().numpy().tobytes())
+
+
+WALK_CASES = [
+    # (name, B, gamma, V): an unaligned vocabulary, a partial last chunk, one exact chunk
+    ("walk-unaligned", 3, 5, 1001),
+    ("walk-partial-chunk", 4, 16, 9000),
+    ("walk-one-chunk", 2, 3, 4096),
+]
+
+
+@pytest.mark.parametrize("case", WALK_CASES, ids=[c[0] for c in WALK_CASES])
+def test_normalizer_walk_matches_full_grid(case):
+    """sd_draft_normalizer with a fixed grid (workgroups > 0, waves walking the items)
+    writes the same workspace bytes as the full grid (workgroups = 0), for kept lengths
+    that skip rows and a chunk that is -inf throughout."""
+    name, B, g, V = case
+    gen = torch.Generator().manual_seed(11)
+    logits = torch.randn((B, g, V), generator=gen).to(torch.bfloat16)
+    logits[0, 0, 4096:] = float("-inf")                 # whole chunks at -inf (V > 4096)
+    logits[-1, 0, :] = float("-inf")                    # a whole row at -inf
+    draft = logits.cuda()
+    vlen = torch.randint(0, g + 1, (B,), generator=gen, dtype=torch.int32)
+    vlen[0], vlen[-1] = g, max(1, int(vlen[-1]))
+    vlen = vlen.cuda()
+    nbytes = sd.accept_workspace_bytes(B, g, V)
+    got = {}
+    for wg in (0, 1, 7, 32):
+        say(name, f"B={B} g={g} V={V} workgroups={wg}")
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        sd.sd_draft_normalizer(draft, vlen, 0.8, ws, workgroups=wg)
+        torch.cuda.synchronize()
+        got[wg] = ws.cpu().numpy()
+    assert got[0].any()
+    for wg in (1, 7, 32):
+        assert np.array_equal(got[wg], got[0]), f"workgroups={wg}"
