@@ -863,6 +863,60 @@ __global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a, int n_mt, int n
 // The LM-head fragment is the MFMA's first operand, so each lane ends with four
 // consecutive vocabulary ids of one row: 16-byte logits stores, and per-row
 // statistics that need two lane exchanges instead of four.
+// Main loop of k_gemm_dma for a wave whose first NV of its TM row tiles hold verified rows
+// (the rest are padding of the last row tile): the DMA issue and the barriers are the
+// same for every NV, so the workgroup's waves stay in step; only the fragment reads and
+// MFMAs of padding row tiles are left out.
+template <int NV, int BM, int BN, int BK, int NS, int NW, int DPT>
+__device__ __forceinline__ void dma_main_loop(uint16_t *S, const uint16_t *const (&src)[DPT], int nk,
+                                              int wave, int lane, int wm, int wn,
+                                              f32x4 (&acc)[BM / 32][BN / (NW / 2) / 16]) {
+  constexpr int WNG = NW / 2, CH = BK / 8, STAGE = (BM + BN) * BK, TN = BN / WNG / 16;
+  auto swz = [](int r) { return (r >> (CH == 4 ? 2 : 1)) & (CH - 1); };
+  auto issue = [&](int kt) {
+    const int kk = min(kt, nk - 1) * BK;            // past the end: reload the last step (unused)
+    LDSP uint16_t *dst = (LDSP uint16_t *)S + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i)
+      __builtin_amdgcn_global_load_lds((const GLBP void *)(src[i] + kk),
+                                       (LDSP void *)(dst + (wave + NW * i) * 512), 16, 0, 0);
+  };
+  const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt is complete once at most (NS-2)*DPT newer DMAs of this thread are pending.
+    constexpr int PEND = (NS - 2) * DPT;
+    __builtin_amdgcn_s_waitcnt((PEND & 15) | (((PEND >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+    lds_barrier();
+    issue(kt + NS - 1);          // refills the buffer read in the previous iteration
+    const LDSP uint16_t *Ab = (const LDSP uint16_t *)S + (kt % NS) * STAGE;
+    const LDSP uint16_t *Bb = Ab + BM * BK;
+    if constexpr (NV > 0) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int c = 4 * ks + fc;
+        bf16x8 af[NV], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int r = wm * (BM / 2) + i * 16 + fr;
+          af[i] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Ab + r * BK + 8 * (c ^ swz(r))));
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const int r = wn * (BN / WNG) + t * 16 + fr;
+          bfr[t] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Bb + r * BK + 8 * (c ^ swz(r))));
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], af[i], acc[i][t], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, int n_nt) {
   constexpr int NT = 64 * NW;                      // threads
@@ -909,56 +963,32 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
     src[i] = row + 8 * c;
   }
   const int nk = d / BK;                            // d % BK == 0 required
-  auto issue = [&](int kt) {
-    const int kk = min(kt, nk - 1) * BK;            // past the end: reload the last step (unused)
-    LDSP uint16_t *dst = (LDSP uint16_t *)S + (kt % NS) * STAGE;
-#pragma unroll
-    for (int i = 0; i < DPT; ++i)
-      __builtin_amdgcn_global_load_lds((const GLBP void *)(src[i] + kk),
-                                       (LDSP void *)(dst + (wave + NW * i) * 512), 16, 0, 0);
-  };
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int fr = lane & 15, fc = lane >> 4;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue(p);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt is complete once at most (NS-2)*DPT newer DMAs of this thread are pending.
-    constexpr int PEND = (NS - 2) * DPT;
-    __builtin_amdgcn_s_waitcnt((PEND & 15) | (((PEND >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-    lds_barrier();
-    issue(kt + NS - 1);          // refills the buffer read in the previous iteration
-    const LDSP uint16_t *Ab = (const LDSP uint16_t *)S + (kt % NS) * STAGE;
-    const LDSP uint16_t *Bb = Ab + BM * BK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int c = 4 * ks + fc;
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * (BM / 2) + i * 16 + fr;
-        af[i] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Ab + r * BK + 8 * (c ^ swz(r))));
-      }
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int r = wn * (BN / WNG) + t * 16 + fr;
-        bfr[t] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Bb + r * BK + 8 * (c ^ swz(r))));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], af[i], acc[i][t], 0, 0, 0);
-    }
+  // Row tiles of this wave that hold verified rows (wave-uniform).
+  const int nv = __builtin_amdgcn_readfirstlane(
+      max(0, min(TM, (M - m0 - wm * (BM / 2) + 15) / 16)));
+  static_assert(TM == 8, "one main-loop instance per count of verified row tiles");
+  switch (nv) {
+    case 8: dma_main_loop<8, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 7: dma_main_loop<7, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 6: dma_main_loop<6, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 5: dma_main_loop<5, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 4: dma_main_loop<4, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 3: dma_main_loop<3, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 2: dma_main_loop<2, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    case 1: dma_main_loop<1, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
+    default: dma_main_loop<0, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): the trailing reloads land before LDS is reused
   __syncthreads();
   // Epilogue from registers. With the LM-head fragment as the MFMA's first operand,
   // lane (fr, fc) holds, for row tile i and vocabulary tile t, row
   // wm * BM/2 + 16 i + fr at the four consecutive ids 16 t + 4 fc .. + 3.
+  const int fr = lane & 15, fc = lane >> 4;
   const int vb = v0 + wn * (BN / WNG) + 4 * fc;
   if (a.logits) {
 #pragma unroll
