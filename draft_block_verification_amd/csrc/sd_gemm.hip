@@ -938,10 +938,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
   const int per = nb / 8, rem = nb % 8, xcd = hb % 8, pos = hb / 8;
   const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + pos;
   const int mt = logical % n_mt, nt = logical / n_mt;
-  const int m0 = mt * BM, v0 = nt * BN;
   const int M = rows_total(a.rm);
   const int d = a.d, V = a.V;
-  if (m0 >= M) return;
+  // The verified rows' 16-row tiles are dealt out as evenly as the row tiles allow (they
+  // differ by at most one 16-row tile), so the row tiles that share an LM-head tile run at
+  // one pace and keep reading it from L2 together. Row tile mt holds rows m0 .. m0 + mr - 1.
+  const int rtiles = (M + 15) / 16, used = (rtiles + 2 * TM - 1) / (2 * TM);
+  if (mt >= used) return;
+  const int rt_base = rtiles / used, rt_extra = rtiles % used;
+  const int m0 = 16 * (mt * rt_base + min(mt, rt_extra)), v0 = nt * BN;
+  const int mr = min(16 * (rt_base + (mt < rt_extra ? 1 : 0)), M - m0);
 
   // DMA i of this thread: wave instruction w + 4 i covers rows RPI*(w + 4 i) .. + RPI - 1;
   // lane l fills LDS slot l: row r = base + l / CH, stored chunk j = l % CH, which holds
@@ -955,7 +961,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
     if (r < BM) {
       const int m = m0 + r;
       int hr = -1;
-      if (m < M) { int rq, jj; hr = hidden_row(a.rm, m, &rq, &jj); }
+      if (r < mr) { int rq, jj; hr = hidden_row(a.rm, m, &rq, &jj); }
       row = a.hidden + (size_t)(hr >= 0 ? hr : 0) * d;
     } else {
       row = a.W + (size_t)min(v0 + r - BM, V - 1) * d;
@@ -969,8 +975,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Row tiles of this wave that hold verified rows (wave-uniform).
-  const int nv = __builtin_amdgcn_readfirstlane(
-      max(0, min(TM, (M - m0 - wm * (BM / 2) + 15) / 16)));
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mr - wm * (BM / 2) + 15) / 16)));
   static_assert(TM == 8, "one main-loop instance per count of verified row tiles");
   switch (nv) {
     case 8: dma_main_loop<8, BM, BN, BK, NS, NW>(S, src, nk, wave, lane, wm, wn, acc); break;
@@ -993,8 +998,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
   if (a.logits) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * (BM / 2) + i * 16 + fr;
-      if (m < M) {
+      const int rl = wm * (BM / 2) + i * 16 + fr, m = m0 + rl;
+      if (rl < mr) {
         float *dst = a.logits + (size_t)m * V;
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
@@ -1050,9 +1055,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
     }
   }
   __syncthreads();
-  for (int rl = tid; rl < BM; rl += NT) {
+  for (int rl = tid; rl < mr; rl += NT) {
     const int m = m0 + rl;
-    if (m >= M) continue;
     const float *x0 = X + rl * 4;
     RowAcc r0{x0[0], x0[1], x0[3], __float_as_int(x0[2])};
     for (int w = 1; w < WNG; ++w) {
