@@ -130,8 +130,8 @@ def main():
     if args.step_times_from_trace:
         return step_times_from_trace(args.step_times_from_trace)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the verify path is measured on one GPU's full-vocabulary share).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the verify path "
+              "runs on one GPU, which holds the whole LM head.", file=sys.stderr)
         sys.exit(2)
 
     import torch
