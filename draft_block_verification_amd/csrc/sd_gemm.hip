@@ -867,6 +867,9 @@ __global__ __launch_bounds__(256) void k_gemm_tile(VerifyArgs a, int n_mt, int n
 // (the rest are padding of the last row tile): the DMA issue and the barriers are the
 // same for every NV, so the workgroup's waves stay in step; only the fragment reads and
 // MFMAs of padding row tiles are left out.
+// A wave raises its priority while it issues a k-step's MFMAs, so that of the two
+// waves sharing a SIMD the one with matrix work ready issues first while the other
+// reads its fragments.
 template <int NV, int BM, int BN, int BK, int NS, int NW, int DPT>
 __device__ __forceinline__ void dma_main_loop(uint16_t *S, const uint16_t *const (&src)[DPT], int nk,
                                               int wave, int lane, int wm, int wn,
@@ -907,11 +910,13 @@ __device__ __forceinline__ void dma_main_loop(uint16_t *S, const uint16_t *const
           const int r = wn * (BN / WNG) + t * 16 + fr;
           bfr[t] = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Bb + r * BK + 8 * (c ^ swz(r))));
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
           for (int t = 0; t < TN; ++t)
             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], af[i], acc[i][t], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   }
