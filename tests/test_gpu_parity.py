@@ -80,6 +80,12 @@ SHAPES = [
     # More vocabulary tiles than the chip holds at once (a second, partial round).
     ("tiled-two-rounds-rej", 5, 16, 64, 70000, 1.0, True),
     ("tiled-two-rounds-greedy", 4, 20, 128, 69999, 0.0, False),
+    # Row counts around the 256-row tile: the verified rows' 16-row tiles are dealt over
+    # the row tiles (255 rows: one tile, last 16-row tile partial; 513: three tiles of
+    # 11/11/11 16-row tiles; 775: four tiles of 13/12/12/12).
+    ("tiled-rows-255", 15, 16, 128, 3000, 1.0, False),
+    ("tiled-rows-513", 27, 18, 64, 2000, 0.0, False),
+    ("tiled-rows-775", 25, 30, 64, 1500, 0.9, False),
 ]
 
 
