@@ -53,6 +53,26 @@ struct RowAcc {
 
 __device__ inline RowAcc row_acc_init() { return RowAcc{-INFINITY, -INFINITY, 0.f, 0x7fffffff}; }
 
+// The value lane l ^ off holds, off = 16 or 32, from gfx950's lane-swap instructions:
+// v_permlane16/32_swap exchange the odd and even 16-lane (32-lane) halves of two
+// registers, so lane l finds lane l ^ off's value in the first result when bit off of l
+// is set and in the second otherwise. One VALU instruction each, no LDS crossbar.
+__device__ inline uint32_t lane_xor_u32(uint32_t x, int off) {
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ inline float lane_xor(float x, int off) { return __uint_as_float(lane_xor_u32(__float_as_uint(x), off)); }
+__device__ inline int lane_xor(int x, int off) { return (int)lane_xor_u32((uint32_t)x, off); }
+__device__ inline double lane_xor(double x, int off) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = lane_xor_u32((uint32_t)b, off), hi = lane_xor_u32((uint32_t)(b >> 32), off);
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
 // Fold a tile's (t1, t2, arg, sum) into a running value; sums are relative to t1.
 __device__ inline void row_acc_merge(RowAcc &r, const RowAcc &o, float scale_log2) {
   const bool win = beats(o.t1, o.arg, r.t1, r.arg);
@@ -602,8 +622,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         }
 #pragma unroll
         for (int off = 16; off <= 32; off <<= 1) {
-          const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-          const int oa = __shfl_xor(a1, off);
+          const float o1 = lane_xor(t1, off), o2 = lane_xor(t2, off);
+          const int oa = lane_xor(a1, off);
           if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
           else { t2 = fmaxf(t2, o1); }
         }
@@ -612,16 +632,21 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             if (vb + q < V) s += exp2f((acc[i][q] - t1) * a.scale_log2);
-          s += __shfl_xor(s, 16);
-          s += __shfl_xor(s, 32);
+          s += lane_xor(s, 16);
+          s += lane_xor(s, 32);
         }
         row_acc_merge(run[i], RowAcc{t1, t2, s, a1}, a.scale_log2);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (zrow >= 0) {
+        // Only lanes < CH hold parts of the dot, except W12's correction lanes.
+        if constexpr (W12) {
+          zacc += lane_xor(zacc, 32);
+          zacc += lane_xor(zacc, 16);
+        }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) zacc += __shfl_xor(zacc, off);
+        for (int off = CH / 2; off >= 1; off >>= 1) zacc += __shfl_xor(zacc, off);
         if (lane == 0) a.zx[zrow] = zacc;
       }
       if (tid == 0 && zmask) {
