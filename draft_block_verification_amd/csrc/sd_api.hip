@@ -144,7 +144,7 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
       return SD_ESHAPE;
     if (!aligned(w12->codes, 16) || !aligned(w12->corr, 16)) return SD_EALIGN;
   }
-  // The slab-blocked bf16 LM head, like W12, is read by the skinny contraction only.
+  // The blocked bf16 LM head, like W12, is read by the skinny contraction only.
   if (blocked && (d % 128 != 0 || (int64_t)B * (gamma + 1) > 64)) return SD_ESHAPE;
   if ((verify_len == nullptr) != (row_offsets == nullptr)) return SD_EINVAL;
   if (!isfinite(temperature) || temperature < 0.f) return SD_EINVAL;
@@ -193,7 +193,7 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
 }
 
 // The three verify calls for any LM-head form: bf16 [V][d] (lm_head), W12 (w12) or the
-// slab-blocked bf16 copy (lm_head with blocked).
+// blocked bf16 copy (lm_head with blocked).
 int32_t verify_logits_impl(const uint16_t *hidden, const uint16_t *lm_head, const sd_w12 *w12,
                            bool blocked, const int32_t *draft_tokens, const int32_t *verify_len,
                            const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
@@ -240,7 +240,7 @@ int32_t verify_greedy_impl(const uint16_t *hidden, const uint16_t *lm_head, cons
                                             (hipStream_t)stream));
 }
 
-// Bytes of the slab-blocked copy of a [V][d] LM head: ceil(V/64) * (d/128) blocks of 16 KB.
+// Bytes of the blocked copy of a [V][d] LM head: ceil(V/64) * (d/128) blocks of 16 KB.
 size_t blocked_bytes(int32_t V, int32_t d) {
   return (size_t)((V + 63) / 64) * (size_t)(d / 128) * 16384u;
 }

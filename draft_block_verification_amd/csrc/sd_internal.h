@@ -102,7 +102,7 @@ __device__ inline bool beats(float va, int ia, float vb, int ib) {
 // Arguments of the LM-head verify kernels (sd_verify_logits).
 struct VerifyArgs {
   const uint16_t *hidden;       // bf16 [B][gamma + 1][d]
-  const uint16_t *W;            // bf16 [V][d], or slab-blocked (w_blocked)
+  const uint16_t *W;            // bf16 [V][d], or the stage-major blocked copy (w_blocked)
   const int32_t *draft_tokens;  // [B][gamma] or null
   const int32_t *verify_len;    // [B] or null
   RowMap rm;
@@ -132,7 +132,7 @@ struct VerifyArgs {
 // LM-head formats of the streaming contraction.
 constexpr int kLmBf16 = 0;      // bf16 [V][d]
 constexpr int kLmW12 = 1;       // W12 groups plus correction slots
-constexpr int kLmBlocked = 2;   // slab-blocked bf16
+constexpr int kLmBlocked = 2;   // stage-major blocked bf16
 
 // Prefix scheduler: one workgroup sorts all R * gamma candidates in LDS.
 constexpr int kSchedMaxCandidates = 16384;

@@ -22,7 +22,7 @@ hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
                               bool *zx_done);
 
-// Slab-blocked copy of a bf16 LM head (the layout VerifyArgs::w_blocked reads).
+// Stage-major blocked copy of a bf16 LM head (the layout VerifyArgs::w_blocked reads).
 hipError_t launch_block_lm_head(const uint16_t *W, int V, int d, uint16_t *out,
                                 hipStream_t stream);
 

@@ -282,7 +282,7 @@ SD_API int32_t sd_verify_greedy_w12(const uint16_t *hidden, const sd_w12 *lm_hea
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Slab-blocked bf16 LM head: the same weights re-laid once so that the streaming
+ * Blocked bf16 LM head: the same weights re-laid once so that the streaming
  * contraction reads each of its stages (64 LM-head rows by 128 columns) as one
  * contiguous 16 KB block. Layout: [d/128][ceil(V/64)][64][128] bf16, stage-major: block
  * (st, s) holds LM-head rows 64 s .. 64 s + 63 at columns 128 st .. 128 st + 127, so the
