@@ -1063,8 +1063,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
       }
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
-      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-      const int oa = __shfl_xor(a1, off);
+      const float o1 = lane_xor(t1, off), o2 = lane_xor(t2, off);
+      const int oa = lane_xor(a1, off);
       if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
       else { t2 = fmaxf(t2, o1); }
     }
@@ -1075,8 +1075,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dma(VerifyArgs a, int n_mt, in
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (vb + t * 16 + q < V) s += exp2f((acc[i][t][q] - t1) * a.scale_log2);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
+      s += lane_xor(s, 16);
+      s += lane_xor(s, 32);
     }
     if (fc == 0) {
       const int rl = wm * (BM / 2) + i * 16 + fr;
