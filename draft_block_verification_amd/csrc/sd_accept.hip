@@ -301,9 +301,11 @@ __global__ __launch_bounds__(64 * kWalkWaves) void k_draft_partial_walk(RejArgs 
   };
   seek();
   if ((V & 7) != 0) {
-    for (; rj < rows; step(), seek()) {
+    while (rj < rows) {
       const DraftPart p = draft_chunk_unaligned(a.draft_logits + (size_t)rj * V, V, c, lane, a.sl);
       if (lane == 0) a.dpart[(size_t)rj * C + c] = p;
+      step();
+      seek();
     }
     return;
   }
