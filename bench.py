@@ -8,10 +8,13 @@ or bonus token. Inputs are staged in HBM before timing; the timed steps run
 as one HIP-graph replay. Verified positions are counted on the GPU (the
 drafts-verified counter, sum over requests of L_r).
 
-Default workload: greedy verify of a 9-token block, B=1, d=2048, V=32768,
-1000 seeded steps. The LM head (134 MB) would otherwise stay resident in the
-256 MB last-level cache between steps; three copies are rotated so every
-step streams it from HBM, as it would behind a real model's layers.
+Default workload: high-concurrency rejection verify, B=128 requests with
+gamma=16 drafts each, d=7168, V=129280, T=1.0, confidence-truncated ragged
+lengths (about 956 verified rows per step), 8 distinct seeded steps staged
+in HBM and cycled. The LM-head contraction is a dense bf16 MFMA problem here
+(about 1.8 TFLOP per step). Smaller LM heads (--workload greedy-block9, 134
+MB) would stay resident in the 256 MB last-level cache between steps, so
+copies are rotated until every step streams its head from HBM.
 
 Prints one JSON line (rank 0).
 """
@@ -40,7 +43,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="greedy-block9")
+    ap.add_argument("--workload", default="concurrency-b128",
+                    help="tiny-greedy, greedy-block9, rejection-b1, ragged-b32 or "
+                         "concurrency-b128 (default)")
     ap.add_argument("--distinct", type=int, default=None,
                     help="distinct pre-staged steps cycled through (default: all for the "
                          "greedy block workload, 8 otherwise)")
@@ -309,28 +314,48 @@ def main():
 
     ms_step = ms_total / K
     value = positions / (ms_total * 1e-3)
+    # The whole step against its own roofline: algorithmic bytes (LM head once, verified
+    # hidden rows, kept drafter rows when T > 0) and flops (2 M V d) of an average timed
+    # step; its roofline time is the larger of bytes / HBM peak and flops / MFMA peak.
+    mean_pos = mean_rows - w.B
+    s_bytes = w_bytes + mean_rows * w.d * 2 + (mean_pos * w.V * 2 if w.T > 0 else 0.0)
+    s_flops = 2.0 * mean_rows * w.V * w.d
+    t_roof = max(s_bytes / (HBM_PEAK_GBS * 1e9), s_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    roof["step_bound"] = ("mfma" if s_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) >=
+                          s_bytes / (HBM_PEAK_GBS * 1e9) else "hbm")
+    roof["step_roofline_us"] = t_roof * 1e6
+    roof["step_frac"] = t_roof / (ms_step * 1e-3)
+    roof["roofline_positions_per_s"] = mean_pos / t_roof
 
     # ---- CPU oracle baseline on a bounded sample of the same steps
     cpu = None
     if args.cpu_seconds > 0:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         from oracle import sd_oracle as O
+        host_cores = len(os.sched_getaffinity(0))
         W64 = O.lm_head_f64(W)
         done_pos, t_cpu, n_cpu = 0, 0.0, 0
-        while t_cpu < args.cpu_seconds and n_cpu < 10 * S:
-            s = steps_host[n_cpu % S]
-            t0 = time.perf_counter()
-            res = O.verify_step(s.hidden, W64, s.draft_tokens, w.T,
-                                conf=s.conf if w.truncate else None, threshold=w.threshold,
-                                draft_logit_bits=s.draft_logits, u_accept=s.u_accept,
-                                u_resample=s.u_resample)
-            t_cpu += time.perf_counter() - t0
-            done_pos += int(res.accept.counters[0])
-            n_cpu += 1
-        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        # The oracle's matmul is the only multi-threaded part; let its BLAS use every
+        # core this process may run on.
+        with threadpool_limits(limits=host_cores, user_api="blas"):
+            blas = [p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"]
+            while t_cpu < args.cpu_seconds and n_cpu < 10 * S:
+                s = steps_host[n_cpu % S]
+                t0 = time.perf_counter()
+                res = O.verify_step(s.hidden, W64, s.draft_tokens, w.T,
+                                    conf=s.conf if w.truncate else None, threshold=w.threshold,
+                                    draft_logit_bits=s.draft_logits, u_accept=s.u_accept,
+                                    u_resample=s.u_resample)
+                t_cpu += time.perf_counter() - t0
+                done_pos += int(res.accept.counters[0])
+                n_cpu += 1
+        del W64
         cpu = {"value": done_pos / t_cpu, "unit": "verified draft positions/s",
-               "cores": int(max(blas) if blas else 1), "kind": "oracle",
-               "sample": f"{n_cpu} steps of {w.name} (fp64 numpy oracle, inputs pre-generated)"}
+               "cores": int(max(blas) if blas else 1), "host_cores": host_cores,
+               "kind": "oracle",
+               "sample": f"{n_cpu} whole steps of {w.name} ({done_pos} verified positions, "
+                         f"{t_cpu:.1f} s; fp64 numpy oracle, inputs pre-generated)"}
 
     out = {
         "metric": "verified draft positions/sec at 1 GPU; % HBM or MFMA roofline",

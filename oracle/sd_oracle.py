@@ -218,6 +218,8 @@ class RejectionDiag:
     cdf_dist: np.ndarray     # float64 [B]: boundary distance of the final draw
     residual: np.ndarray     # bool [B]: correction drawn from the residual (else bonus / p)
     mass: np.ndarray         # float64 [B]: S of the final draw
+    cdf_conc: np.ndarray     # float64 [B]: sqrt(sum_v (w_v / S)^2) of the final draw's weights
+    draw_row: np.ndarray     # int64 [B]: packed row the final draw was taken from
 
 
 def accept_rejection(z: np.ndarray, draft_logit_bits: np.ndarray, draft_tokens: np.ndarray,
@@ -243,6 +245,8 @@ def accept_rejection(z: np.ndarray, draft_logit_bits: np.ndarray, draft_tokens: 
     cdf_dist = np.zeros(B)
     residual = np.zeros(B, dtype=bool)
     mass = np.zeros(B)
+    cdf_conc = np.zeros(B)
+    draw_row = np.zeros(B, dtype=np.int64)
     for r in range(B):
         base, L = int(row_offsets[r]), int(verify_len[r])
         lq = bf16_decode(draft_logit_bits[r, :L]) / T          # [L][V]
@@ -258,19 +262,23 @@ def accept_rejection(z: np.ndarray, draft_logit_bits: np.ndarray, draft_tokens: 
             if a == L and not float(u_accept[r, j]) < min(1.0, p / q):
                 a = j          # first rejection; later rows only fill the diagnostics
         acc[r] = a
+        draw_row[r] = base + a
         p_row = np.exp(z[base + a] / T - lse_p[base + a])
         u = float(u_resample[r, a])
+        weights = p_row
         if a < L:
             q_row = np.exp(lq[a] - lse_q[r, a])
             R = np.maximum(0.0, p_row - q_row)
             if np.any(R > 0):
-                nxt[r], mass[r], cdf_dist[r] = inverse_cdf(R, u)
+                weights = R
                 residual[r] = True
-                continue
-        nxt[r], mass[r], cdf_dist[r] = inverse_cdf(p_row, u)
+        nxt[r], mass[r], cdf_dist[r] = inverse_cdf(weights, u)
+        # How concentrated the draw's weights are: the spread of a CDF value under
+        # independent relative errors of the weights scales with this (diagnostic only).
+        cdf_conc[r] = float(np.sqrt(np.sum((weights / mass[r]) ** 2))) if mass[r] > 0 else 0.0
     counters = np.array([int(np.sum(verify_len)), int(np.sum(acc))], dtype=np.int64)
-    return AcceptResult(acc, nxt, counters), RejectionDiag(ratio, p_x, q_x, lse_q,
-                                                           cdf_dist, residual, mass)
+    return AcceptResult(acc, nxt, counters), RejectionDiag(ratio, p_x, q_x, lse_q, cdf_dist,
+                                                           residual, mass, cdf_conc, draw_row)
 
 
 def acceptance_rate(z: np.ndarray, draft_logit_bits: np.ndarray, verify_len: np.ndarray,

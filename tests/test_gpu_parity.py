@@ -16,8 +16,8 @@ import draft_block_verification_amd as sd
 from oracle import sd_oracle as O
 from synth import make_step, make_weights, workload
 
-from _parity import (Report, attach_inputs, bf16_dev, check_logits_rows, compare, run_gpu,
-                     run_oracle, slice_step, upload_step)
+from _parity import (Report, attach_inputs, bf16_dev, check_logits_rows, compare, lm_head,
+                     run_gpu, run_oracle, upload_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,10 @@ def need_gpu():
     yield
 
 
-def full_case(w, steps, seed=0, check_all_logits=True):
-    """Oracle over whole batches: every request and every logit compared."""
+def full_case(w, steps, seed=0, check_all_logits=True, named=False):
+    """Oracle over whole batches: every request and every logit compared. On the named
+    workloads (named=True) no exemption may be used: every accepted length, token and
+    argmax equals the oracle's."""
     W = make_weights(w, seed)
     W64 = O.lm_head_f64(W)
     W_dev = bf16_dev(W)
@@ -52,6 +54,8 @@ def full_case(w, steps, seed=0, check_all_logits=True):
             check_logits_rows(w, g.logits, o.z, rep)
         assert np.array_equal(g.counters, o.accept.counters)
     say("report", rep)
+    if named:
+        assert rep.exempt == 0, rep
     return rep
 
 
@@ -131,49 +135,46 @@ def test_rows_beyond_one_grid_dimension(case):
 
 def test_workload_tiny_greedy_all_steps():
     w = workload("tiny-greedy")
-    rep = full_case(w, steps=range(w.steps))
+    rep = full_case(w, steps=range(w.steps), named=True)
     assert rep.requests == 1000
 
 
 def test_workload_greedy_block9():
     w = workload("greedy-block9")
-    full_case(w, steps=range(100))
+    rep = full_case(w, steps=range(w.steps), named=True)
+    assert rep.requests == w.steps
 
 
 def test_workload_rejection_b1():
     w = workload("rejection-b1")
-    full_case(w, steps=range(10))
+    full_case(w, steps=range(10), named=True)
 
 
 def test_workload_ragged_b32():
     w = workload("ragged-b32")
-    full_case(w, steps=range(4))
+    full_case(w, steps=range(4), named=True)
 
 
-def test_workload_concurrency_b128_sampled():
-    """Full size (W 1.85 GB); the oracle computes a sample of requests exactly."""
+def test_workload_concurrency_b128():
+    """Full size (W 1.85 GB): every request of two steps, every logit row, the row
+    statistics and the batch counters against the oracle."""
     w = workload("concurrency-b128")
-    W = make_weights(w)
-    W_dev = bf16_dev(W)
-    W64 = O.lm_head_f64(W)
+    W, W64, W_dev = lm_head(w)
     vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold)
     rep = Report()
-    rng = np.random.default_rng(99)
     for st in range(2):
-        say(w.name, f"step={st} sampled")
+        say(w.name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={st} whole batch")
         s = make_step(w, W, st)
-        ds = upload_step(s)
-        g = run_gpu(w, W_dev, ds, vr)
-        assert g.flags == 0
-        req = sorted(set(rng.choice(w.B, 6, replace=False).tolist()) | {0, w.B - 1})
-        o = attach_inputs(run_oracle(w, W64, slice_step(s, req)), slice_step(s, req))
-        compare(w, g, o, req, rep)
-        rows = [int(g.row_offsets[r]) + j for r in req for j in range(int(g.verify_len[r]) + 1)]
-        idx = torch.as_tensor(rows, dtype=torch.long, device=vr.logits.device)
-        check_logits_rows(w, vr.logits.index_select(0, idx).cpu().numpy(), o.z, rep)
-        # Counters cover the whole batch: compare with the GPU's own per-request outputs.
-        assert g.counters[0] == g.verify_len.sum() and g.counters[1] == g.accept_len.sum()
+        g = run_gpu(w, W_dev, upload_step(s), vr, fetch_all_logits=True)
+        assert g.flags == 0, f"device flags {g.flags}"
+        o = attach_inputs(run_oracle(w, W64, s), s)
+        compare(w, g, o, range(w.B), rep)
+        check_logits_rows(w, g.logits, o.z, rep)
+        assert np.array_equal(g.counters, o.accept.counters)
+        del g, o
     say("report", rep)
+    assert rep.requests == 2 * w.B
+    assert rep.exempt == 0, rep
 
 
 # --------------------------------------------------------------- properties
