@@ -11,7 +11,7 @@ from ._lib import (EXPORTED, FLAG_NO_RESIDUAL, FLAG_ROW_OFFSETS, FLAG_VERIFY_LEN
                    sd_accept_rejection_ex, sd_accept_rejection_prenormalized,
                    sd_draft_normalizer, sd_schedule_prefix, sd_truncate_by_confidence,
                    sd_verify_contraction, sd_verify_contraction_w12, sd_verify_greedy,
-                   sd_verify_greedy_w12,
+                   sd_verify_greedy_noalloc, sd_verify_greedy_w12, NOALLOC_SCRATCH_BYTES,
                    sd_verify_logits, sd_verify_logits_w12, stats_to_numpy, verify_workspace_bytes,
                    w12_encode)
 
@@ -22,5 +22,6 @@ __all__ = ["EXPORTED", "FLAG_NO_RESIDUAL", "FLAG_ROW_OFFSETS", "FLAG_VERIFY_LEN"
            "sd_accept_rejection_ex", "sd_accept_rejection_prenormalized", "sd_draft_normalizer",
            "sd_schedule_prefix", "sd_truncate_by_confidence",
            "sd_verify_contraction", "sd_verify_contraction_w12", "sd_verify_greedy",
-           "sd_verify_greedy_w12", "sd_verify_logits",
+           "sd_verify_greedy_noalloc", "sd_verify_greedy_w12", "NOALLOC_SCRATCH_BYTES",
+           "sd_verify_logits",
            "sd_verify_logits_w12", "stats_to_numpy", "verify_workspace_bytes", "w12_encode"]

@@ -55,6 +55,8 @@ _SIGS = {
                                      _vp]),
     "sd_verify_greedy": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                 _vp, _sz, _vp]),
+    "sd_verify_greedy_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                        _vp, _vp, _vp, _vp]),
     "sd_accept_greedy": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sd_accept_rejection": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -435,6 +437,47 @@ def sd_verify_greedy(hidden: torch.Tensor, lm_head: torch.Tensor, draft_tokens: 
                                      _ptr(row_offsets), B, g, d, V, _ptr(stats), _ptr(accept_len),
                                      _ptr(next_token), _ptr(counters), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
+    return stats, accept_len, next_token
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sd_verify_greedy_noalloc(hidden: torch.Tensor, lm_head: torch.Tensor,
+                             draft_tokens: torch.Tensor, verify_len: Optional[torch.Tensor] = None,
+                             row_offsets: Optional[torch.Tensor] = None,
+                             stats: torch.Tensor = None, accept_len: torch.Tensor = None,
+                             next_token: torch.Tensor = None,
+                             counters: Optional[torch.Tensor] = None,
+                             flags: Optional[torch.Tensor] = None, stream=None):
+    """sd_verify_greedy with the library's own per-GPU scratch instead of a workspace.
+    The caller passes every output (stats, accept_len, next_token; counters and the
+    uint32 flag word optional), so the call allocates nothing; bf16 [V][d] LM head."""
+    _need(hidden, "hidden", torch.bfloat16)
+    B, g1, d = hidden.shape
+    g = g1 - 1
+    _need(lm_head, "lm_head", torch.bfloat16)
+    V = lm_head.shape[0]
+    _need(lm_head, "lm_head", torch.bfloat16, (V, d))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
+    if verify_len is not None:
+        _need(verify_len, "verify_len", torch.int32, (B,))
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    if stats is None or accept_len is None or next_token is None:
+        raise ValueError("sd_verify_greedy_noalloc: pass stats, accept_len and next_token")
+    _need(stats, "stats", torch.int64, (B * g1, 4))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _need(next_token, "next_token", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+    _check("sd_verify_greedy_noalloc",
+           _lib.sd_verify_greedy_noalloc(_ptr(hidden), _ptr(lm_head), _ptr(draft_tokens),
+                                         _ptr(verify_len), _ptr(row_offsets), B, g, d, V,
+                                         _ptr(stats), _ptr(accept_len), _ptr(next_token),
+                                         _ptr(counters), _ptr(flags), _stream(stream)))
     return stats, accept_len, next_token
 
 

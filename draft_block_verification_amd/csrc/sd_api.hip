@@ -3,9 +3,16 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sd_launch.h"
 
 using namespace sdv;
+
+// Scratch of sd_verify_greedy_noalloc: the verify workspace for callers that cannot
+// allocate. One copy per GPU, at its own address on each; host code uses only the
+// address looked up per device (scratch_address), never this name.
+static __device__ __align__(256) uint8_t scratch[SD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -49,6 +56,31 @@ hipError_t clear_words(void *p, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void k_copy_word(const uint32_t *src, uint32_t *dst) { *dst = *src; }
+
+// Device address of `scratch` on the current device, looked up on the first call made
+// with that device current and kept for the process.
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +95,7 @@ const char *sd_status_string(int32_t status) {
     case SD_EALIGN: return "misaligned tensor pointer";
     case SD_EWORKSPACE: return "workspace missing or too small";
     case SD_EDEVICE: return "HIP launch or copy failed";
+    case SD_ESCRATCH: return "problem exceeds the allocation-free scratch (SD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -278,6 +311,46 @@ int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
   return verify_greedy_impl(hidden, lm_head, nullptr, false, draft_tokens, verify_len,
                             row_offsets, B, gamma, d, V, stats, accept_len, next_token, counters,
                             workspace, workspace_bytes, stream);
+}
+
+int32_t sd_verify_greedy_noalloc(const uint16_t *hidden, const uint16_t *lm_head,
+                                 const int32_t *draft_tokens, const int32_t *verify_len,
+                                 const int32_t *row_offsets, int32_t B, int32_t gamma, int32_t d,
+                                 int32_t V, sd_row_stats *stats, int32_t *accept_len,
+                                 int32_t *next_token, int64_t *counters, uint32_t *flags,
+                                 void *stream) {
+  // Every host check before the scratch lookup, so bad arguments never touch the runtime.
+  if (!lm_head || !draft_tokens || !accept_len || !next_token) return SD_EINVAL;
+  const int32_t sz = check_sizes(B, gamma, d, V);
+  if (sz != SD_OK) return sz;
+  if (verify_ws_bytes(B, gamma, V) > SD_NOALLOC_SCRATCH_BYTES) return SD_ESCRATCH;
+  if (!aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (flags && !aligned(flags, 4)))
+    return SD_EALIGN;
+  VerifyArgs a;
+  // The setup checks run against a stand-in workspace address (never dereferenced on the
+  // host); the real scratch address replaces it below.
+  void *const probe = reinterpret_cast<void *>((uintptr_t)1 << 12);
+  int32_t st = verify_setup(hidden, lm_head, nullptr, false, draft_tokens, verify_len, row_offsets,
+                            B, gamma, d, V, 0.f, nullptr, stats, true, probe,
+                            SD_NOALLOC_SCRATCH_BYTES, &a);
+  if (st != SD_OK) return st;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return SD_EDEVICE;
+  st = verify_setup(hidden, lm_head, nullptr, false, draft_tokens, verify_len, row_offsets, B,
+                    gamma, d, V, 0.f, nullptr, stats, true, ws, SD_NOALLOC_SCRATCH_BYTES, &a);
+  if (st != SD_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // The header (sticky flags, arrival ticket) starts every call at zero; partials and
+  // drafted-token logits are written in full by the contraction before they are read.
+  if (clear_words(ws, sizeof(WsHeader) / 4, s) != hipSuccess) return SD_EDEVICE;
+  hipError_t e = launch_verify_greedy(a, accept_len, next_token, counters, s);
+  if (e == hipSuccess && flags) {
+    hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(1), 0, s, reinterpret_cast<const uint32_t *>(ws),
+                       flags);
+    e = hipGetLastError();
+  }
+  return launch_status(e);
 }
 
 int32_t sd_verify_logits_w12(const uint16_t *hidden, const sd_w12 *lm_head,

@@ -68,7 +68,9 @@ enum {
     SD_ESHAPE = 2,      /* B < 1, gamma outside [1, 64], d % 8 != 0, V < 1, size overflow */
     SD_EALIGN = 3,      /* a bf16 / fp32 tensor not 16-byte aligned, stats not 8-byte aligned */
     SD_EWORKSPACE = 4,  /* workspace pointer null or smaller than required       */
-    SD_EDEVICE = 5      /* a HIP launch or copy failed                           */
+    SD_EDEVICE = 5,     /* a HIP launch or copy failed                           */
+    SD_ESCRATCH = 6     /* the problem needs more scratch than the allocation-free
+                           entry point holds (SD_NOALLOC_SCRATCH_BYTES)            */
 };
 
 /* Sticky device flags (bit mask) accumulated in a workspace. */
@@ -216,6 +218,36 @@ SD_API int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
                                 int32_t V, sd_row_stats *stats, int32_t *accept_len,
                                 int32_t *next_token, int64_t *counters, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * sd_verify_greedy for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc. The verify
+ * workspace (header, per-tile row partials, drafted-token logits) lives in a file-scope
+ * device array of the library, SD_NOALLOC_SCRATCH_BYTES bytes on every GPU the library
+ * runs on, held until the process ends; its address is looked up once per device on
+ * the first call made with that device current. The call itself allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ *   hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma, d, V, stats,
+ *   accept_len, next_token, counters   as for sd_verify_greedy (bf16 [V][d] LM head)
+ *   flags   device uint32 [1] out, 4-byte aligned, or NULL: this call's sticky device
+ *           flag word (SD_FLAG_*); the scratch header is cleared at the start of every
+ *           call, so flags cover this call only
+ *   stream  hipStream_t of the device that is current at the call
+ * Limit: sd_verify_workspace_bytes(B, gamma, d, V) <= SD_NOALLOC_SCRATCH_BYTES, else
+ * SD_ESCRATCH before any GPU work (16 MiB holds, for example, 64 rows at V = 151936 or
+ * 400 rows at V = 32768). Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be serialised
+ * by the caller. Outputs are the bytes sd_verify_greedy writes for the same inputs.
+ * Errors: as for sd_verify_greedy (SD_EWORKSPACE does not occur), SD_ESCRATCH, and
+ * SD_EDEVICE when the scratch address cannot be looked up.
+ */
+#define SD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+SD_API int32_t sd_verify_greedy_noalloc(const uint16_t *hidden, const uint16_t *lm_head,
+                                        const int32_t *draft_tokens, const int32_t *verify_len,
+                                        const int32_t *row_offsets, int32_t B, int32_t gamma,
+                                        int32_t d, int32_t V, sd_row_stats *stats,
+                                        int32_t *accept_len, int32_t *next_token,
+                                        int64_t *counters, uint32_t *flags, void *stream);
 
 /*
  * W12 LM head (SpecPilot page, "Reasons": a lossless 12-bit weight format whose three

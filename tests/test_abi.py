@@ -37,6 +37,7 @@ def test_abi_version_and_status_strings():
     lib.sd_status_string.restype = ctypes.c_char_p
     assert lib.sd_status_string(0) == b"ok"
     assert b"workspace" in lib.sd_status_string(4)
+    assert b"scratch" in lib.sd_status_string(6)
     assert lib.sd_status_string(99) == b"unknown status"
 
 
@@ -199,3 +200,32 @@ def test_schedule_prefix_host_validation():
     assert call(R=1025, g=16, n=1025 * 17 + 1) == 2  # more than 16384 candidates
     assert call(conf=MISALIGNED) == 3
     assert call(stale=MISALIGNED, mode=1) == 3
+
+
+def _noalloc(**kw):
+    a = dict(hidden=FAKE, lm_head=FAKE, draft=FAKE, vlen=None, offs=None, B=1, g=9, d=2048,
+             V=32768, stats=FAKE, acc=FAKE, nxt=FAKE, counters=None, flags=None, stream=None)
+    a.update(kw)
+    f = lib.sd_verify_greedy_noalloc
+    f.restype = ctypes.c_int32
+    return f(a["hidden"], a["lm_head"], a["draft"], a["vlen"], a["offs"], ctypes.c_int32(a["B"]),
+             ctypes.c_int32(a["g"]), ctypes.c_int32(a["d"]), ctypes.c_int32(a["V"]), a["stats"],
+             a["acc"], a["nxt"], a["counters"], a["flags"], a["stream"])
+
+
+def test_verify_greedy_noalloc_host_validation():
+    """Every argument error, and a problem too large for the fixed scratch, is reported
+    before the library looks up its scratch or launches anything."""
+    assert _noalloc(hidden=None) == 1
+    assert _noalloc(lm_head=None) == 1
+    assert _noalloc(draft=None) == 1
+    assert _noalloc(acc=None) == 1
+    assert _noalloc(vlen=FAKE) == 1                   # lengths without offsets
+    assert _noalloc(g=65) == 2
+    assert _noalloc(d=12) == 2
+    assert _noalloc(hidden=MISALIGNED) == 3
+    assert _noalloc(flags=MISALIGNED) == 3
+    # 16 MiB of scratch: the config-4 shape needs about 21 MB of row partials.
+    assert sd.verify_workspace_bytes(32, 16, 4096, 151936) > sd.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(B=32, g=16, d=4096, V=151936) == 6
+    assert sd.verify_workspace_bytes(1, 9, 2048, 32768) <= sd.NOALLOC_SCRATCH_BYTES
