@@ -265,68 +265,6 @@ __global__ __launch_bounds__(64 * kDraftWaves) void k_draft_partial(RejArgs a) {
   }
 }
 
-// Bounded footprint, for running beside the contraction on another stream: a fixed grid
-// of 16-wave workgroups whose waves walk the (draft row, chunk) items in row-major order
-// with a stride of the grid's wave count, skipping rows past L_r, with the next item's
-// loads in flight while the current one is reduced. Many waves per workgroup keep the
-// work on few compute units (workgroups reach the XCDs in turn, so a grid of one per XCD
-// holds one compute unit on each). Same partials, bit for bit, as k_draft_partial.
-constexpr int kWalkWaves = 16;
-
-__global__ __launch_bounds__(64 * kWalkWaves) void k_draft_partial_walk(RejArgs a) {
-  const int gamma = a.rm.gamma, C = a.C, V = a.V, lane = threadIdx.x & 63;
-  const int rows = a.rm.B * gamma;
-  // The walk state is wave-uniform; readfirstlane keeps it in scalar registers, so the
-  // kept-length lookups are scalar loads that do not wait on the vector loads in flight.
-  const int nw = gridDim.x * kWalkWaves;
-  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWalkWaves + (threadIdx.x >> 6));
-  const int dq = nw / C, dr = nw % C;
-  int rj = gw / C, c = gw % C;
-  int r_seen = -1, L_seen = 0;      // kept length of the last request looked up
-  auto step = [&]() {
-    rj += dq;
-    c += dr;
-    if (c >= C) { c -= C; ++rj; }
-  };
-  auto seek = [&]() {        // advance (rj, c) to the first item of a kept row, or rj >= rows
-    while (rj < rows) {
-      const int r = rj / gamma;
-      if (r != r_seen) {
-        r_seen = r;
-        L_seen = clamp_len(a.verify_len, r, gamma, lane == 0 ? a.ws : nullptr);
-      }
-      if (rj - r * gamma < L_seen) return;
-      step();
-    }
-  };
-  seek();
-  if ((V & 7) != 0) {
-    while (rj < rows) {
-      const DraftPart p = draft_chunk_unaligned(a.draft_logits + (size_t)rj * V, V, c, lane, a.sl);
-      if (lane == 0) a.dpart[(size_t)rj * C + c] = p;
-      step();
-      seek();
-    }
-    return;
-  }
-  u32x4 w[8];
-  if (rj < rows) draft_chunk_load(a.draft_logits + (size_t)rj * V, V, c, lane, w);
-  while (rj < rows) {
-    const int cur_rj = rj, cur_c = c;
-    step();
-    seek();
-    // Next item's loads (past the end: the current item again, never used), issued on
-    // every path so the wait before the reduction below leaves them in flight.
-    const int nrj = rj < rows ? rj : cur_rj, nc = rj < rows ? c : cur_c;
-    u32x4 wn[8];
-    draft_chunk_load(a.draft_logits + (size_t)nrj * V, V, nc, lane, wn);
-    const DraftPart p = draft_chunk_stats(w, a.sl);
-    if (lane == 0) a.dpart[(size_t)cur_rj * C + cur_c] = p;
-#pragma unroll
-    for (int h = 0; h < 8; ++h) w[h] = wn[h];
-  }
-}
-
 // One workgroup per request; 16 lanes per draft row (16 rows per pass). A row's
 // token, statistics, uniform and chunk partials are loaded together, the drafted
 // token's drafter logit as soon as its id is known.
@@ -787,26 +725,13 @@ RejArgs rej_args(const uint16_t *draft_logits, const int32_t *verify_len, const 
 
 }  // namespace
 
-hipError_t launch_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
-                                   int B, int gamma, int V, float temperature, void *workspace,
-                                   int workgroups, hipStream_t stream) {
-  const RowMap rm{nullptr, B, gamma};
-  const RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
-  if (workgroups > 0)
-    hipLaunchKernelGGL(k_draft_partial_walk, dim3(workgroups), dim3(64 * kWalkWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_draft_partial, dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(B * gamma)),
-                       dim3(64 * kDraftWaves), 0, stream, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,
                                    const uint16_t *draft_logits, const int32_t *draft_tokens,
                                    const int32_t *verify_len, const RowMap &rm,
                                    const float *u_accept, const float *u_resample, int V,
                                    float temperature, int32_t *accept_len, int32_t *next_token,
                                    int64_t *counters, double *accept_rate, void *workspace,
-                                   bool normalized, hipStream_t stream) {
+                                   hipStream_t stream) {
   RejArgs a = rej_args(draft_logits, verify_len, rm, V, temperature, workspace);
   a.logits = logits;
   a.stats = stats;
@@ -821,12 +746,10 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
   a.rate_part = accept_rate ? reinterpret_cast<double *>(a.dpart) : nullptr;
   a.rate = accept_rate;
   hipError_t e;
-  if (!normalized) {
-    hipLaunchKernelGGL(k_draft_partial,
-                       dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(rm.B * rm.gamma)),
-                       dim3(64 * kDraftWaves), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(k_draft_partial,
+                     dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(rm.B * rm.gamma)),
+                     dim3(64 * kDraftWaves), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int draw_rows = rm.B + (accept_rate ? rm.B * rm.gamma : 0);

@@ -427,48 +427,6 @@ SD_API int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *s
                             int32_t *next_token, int64_t *counters, double *accept_rate,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/*
- * The drafter-row normaliser of sd_accept_rejection on its own (DSpark summary,
- * "Problem definition": q_j = softmax(draft_logits[r][j] / T) needs the log-sum-exp of
- * every kept drafter row). It reads only the drafter logits and the kept lengths, not
- * the target's verify outputs, so a caller may run it on a second stream while
- * sd_verify_logits runs, then finish with sd_accept_rejection_prenormalized.
- *   draft_logits bf16 [B][gamma][V], 16-byte aligned
- *   verify_len   int32 [B] kept drafts L_r (clamped into [0, gamma], flagged), or NULL
- *                for L_r = gamma
- *   temperature  > 0, the one the acceptance call will get
- *   workspace    the accept workspace (sd_accept_workspace_bytes(B, gamma, V) bytes,
- *                256-byte aligned); this call writes its drafter chunk partials
- *   workgroups   0: one wave per (4096-id chunk, kept row) over a grid as large as the
- *                rows need, the fastest form on an idle GPU; 1 .. 65535: exactly that
- *                many workgroups of 1024 threads, whose waves walk the (row, chunk) items
- *                in turn. The second form bounds how much of the GPU the call holds, so
- *                that beside sd_verify_logits on another stream it fills compute units
- *                the contraction leaves idle instead of delaying it. The partials are the
- *                same bytes either way.
- * Errors: SD_EINVAL (null drafter logits, temperature not finite and positive,
- * workgroups outside [0, 65535]), SD_ESHAPE, SD_EALIGN, SD_EWORKSPACE, SD_EDEVICE.
- * Rows j >= L_r are not read.
- */
-SD_API int32_t sd_draft_normalizer(const uint16_t *draft_logits, const int32_t *verify_len,
-                                   int32_t B, int32_t gamma, int32_t V, float temperature,
-                                   void *workspace, size_t workspace_bytes, int32_t workgroups,
-                                   void *stream);
-
-/*
- * sd_accept_rejection_ex without its drafter-row normaliser: the workspace must hold
- * what sd_draft_normalizer wrote for the same draft_logits, verify_len, B, gamma, V and
- * temperature, with no other call on that workspace in between, and that call must be
- * ordered before this one (same stream, or an event). Arguments, outputs and errors
- * are those of sd_accept_rejection_ex, and so are the output bytes.
- */
-SD_API int32_t sd_accept_rejection_prenormalized(
-    const float *logits, const sd_row_stats *stats, const uint16_t *draft_logits,
-    const int32_t *draft_tokens, const int32_t *verify_len, const int32_t *row_offsets,
-    const float *u_accept, const float *u_resample, int32_t B, int32_t gamma, int32_t V,
-    float temperature, int32_t *accept_len, int32_t *next_token, int64_t *counters,
-    double *accept_rate, void *workspace, size_t workspace_bytes, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

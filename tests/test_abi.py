@@ -121,42 +121,6 @@ def test_accept_rejection_ex_host_validation():
     assert r(*small_ws) == 4
 
 
-def test_draft_normalizer_and_prenormalized_host_validation():
-    n = lib.sd_draft_normalizer
-    args = [FAKE, None, 1, 4, 1024, ctypes.c_float(1.0), FAKE, ctypes.c_size_t(1 << 20), 0, None]
-    bad = list(args)
-    bad[0] = None
-    assert n(*bad) == 1                               # drafter logits required
-    for wg in (-1, 65536):
-        bad = list(args)
-        bad[8] = wg
-        assert n(*bad) == 1                           # workgroups outside [0, 65535]
-    bad = list(args)
-    bad[5] = ctypes.c_float(float("nan"))
-    assert n(*bad) == 1
-    bad = list(args)
-    bad[3] = 65
-    assert n(*bad) == 2                               # gamma past 64
-    bad = list(args)
-    bad[1] = ctypes.c_void_p(0x10002)
-    assert n(*bad) == 3                               # verify_len not 4-byte aligned
-    bad = list(args)
-    bad[7] = ctypes.c_size_t(64)
-    assert n(*bad) == 4
-    r = lib.sd_accept_rejection_prenormalized
-    args = [FAKE] * 8 + [1, 4, 1024, ctypes.c_float(1.0)] + [FAKE, FAKE, None, None, FAKE,
-                                                             ctypes.c_size_t(1 << 20), None]
-    bad = list(args)
-    bad[4] = None                                     # verify_len without row_offsets
-    assert r(*bad) == 1
-    bad = list(args)
-    bad[15] = ctypes.c_void_p(0x10004)
-    assert r(*bad) == 3
-    bad = list(args)
-    bad[17] = ctypes.c_size_t(64)
-    assert r(*bad) == 4
-
-
 def test_lm_head_block_host_validation():
     assert lib.sd_lm_head_block_bytes(1000, 256) == 16 * 2 * 16384
     assert lib.sd_lm_head_block_bytes(64, 128) == 16384
