@@ -312,6 +312,12 @@ __device__ inline u32x4 w12_decode8(uint32_t l0, uint32_t l1, uint32_t n, uint32
                __builtin_amdgcn_perm(h1, l1, 0x05010400u), __builtin_amdgcn_perm(h1, l1, 0x07030602u)};
 }
 
+// Block permutation of a W12 stage row in LDS: the row's four 48-byte blocks (four
+// 12-byte groups each) are stored at block b ^ w12_block_swz(row). A fragment read takes
+// one group from each of 16 consecutive rows; with 192-byte rows those rows repeat every
+// four in the 64 banks, and the permutation spreads them over all of them.
+__device__ inline int w12_block_swz(int row) { return (row >> 2) & 3; }
+
 // Byte offset of group c of LM-head row x in the region-blocked W12 layout.
 __device__ inline size_t w12_group_offset(int x, int c, int nst) {
   return ((((size_t)(x >> 6) * nst + (c >> 4)) * 64 + (x & 63)) * 16 + (c & 15)) * 12;
@@ -425,7 +431,14 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   const uint16_t *h_src[HI];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    if (W12 || BLK) {
+    if (W12) {
+      // LDS piece u (16 bytes) of the slab's 12 KB: row u / 12, piece u % 12 of its 192
+      // bytes. Within a row, blocks of three pieces (four 12-byte groups) are permuted
+      // by w12_block_swz, so the 16 rows a fragment read touches hit 64 different banks.
+      const int u = 64 * (wave + 4 * i) + lane, row = u / 12, pc = u % 12;
+      w_row[i] = 0;
+      w_off[i] = 16 * (row * 12 + 3 * ((pc / 3) ^ w12_block_swz(row)) + pc % 3);
+    } else if (BLK) {
       w_row[i] = 0;                           // the region is contiguous: piece u at 16 u
       w_off[i] = 16 * (64 * (wave + 4 * i) + lane);
     } else {
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
       const int c = 4 * s + fc;
       bf16x8 b;
       if (W12) {
-        const int o = (br * KC * 3 / 2 + 12 * c) / 4;
+        const int o = (br * KC * 3 / 2 + 12 * (c ^ (4 * w12_block_swz(br)))) / 4;
         u32x4 w = w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1);
         // A corrected weight is coded as a signed zero; the lane holding its row and
         // 8-column chunk puts the exact bits in its place before the MFMA.
@@ -576,7 +589,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         const u32x4 hv = *(const LDSP u32x4 *)(Hb + zrow * KC + 8 * (lane ^ (zrow & 15)));
         u32x4 wv;
         if (W12) {
-          const int o = (zw * KC * 3 / 2 + 12 * lane) / 4;
+          const int o = (zw * KC * 3 / 2 + 12 * (lane ^ (4 * w12_block_swz(zw)))) / 4;
           wv = w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1);
         } else {
           wv = *(const LDSP u32x4 *)(Sb + zw * KC + 8 * (lane ^ (zw & 15)));
