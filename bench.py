@@ -62,11 +62,12 @@ def parse():
                     help="truncating workloads: confidence threshold (default) or the "
                          "hardware-aware prefix scheduler on an SPS table profiled at start "
                          "(top-k sizes the batch from the confidences of two steps before)")
-    ap.add_argument("--weights", choices=["bf16", "w12", "blocked"], default="bf16",
+    ap.add_argument("--weights", choices=["auto", "bf16", "w12", "blocked"], default="auto",
                     help="LM-head format: bf16 [V][d]; the lossless W12 stream (encoded on the "
                          "host before timing); or the same bf16 weights re-laid in 64x128 slab "
                          "blocks (sd_lm_head_block, before timing). w12 and blocked: streaming "
-                         "regime only")
+                         "regime only. auto (default): blocked in the streaming regime "
+                         "(B (gamma + 1) <= 64, d % 128 == 0), else bf16")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the verify benchmark: the toy multi-step decode loop "
                          "(bigram target over the workload's LM head, drafter table right 75%% "
@@ -149,6 +150,12 @@ def main():
 
     def bf16_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.weights == "auto":
+        # The blocked copy is a one-time re-layout of static weights that the streaming
+        # contraction reads as contiguous stages; the tiled regime reads [V][d].
+        streaming = w.B * (w.gamma + 1) <= 64 and w.d % 128 == 0
+        args.weights = "blocked" if streaming else "bf16"
 
     # ---- stage inputs in HBM
     W = make_weights(w)
