@@ -193,6 +193,7 @@ int32_t verify_setup(const uint16_t *hidden, const uint16_t *lm_head, const sd_w
   int part_stride = 0;
   verify_workspace_layout(B, gamma, V, &part_off, &part_stride, &zx_off);
   char *wsb = reinterpret_cast<char *>(workspace);
+  *out = VerifyArgs{};
   VerifyArgs &a = *out;
   a.hidden = hidden;
   a.W = w12 ? nullptr : lm_head;

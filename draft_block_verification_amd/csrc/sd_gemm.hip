@@ -375,6 +375,99 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
   return part;
 }
 
+// Greedy verify tail of request r, by the workgroup's nw waves (one wave per row):
+// merges the n partials of each of its rows 0..L_r, writes their statistics with the
+// drafted token's exact logit, then finds the first row whose argmax differs from the
+// draft and emits that row's argmax (LFM2.5-DSpark blog, "Quality parity"). s_arg[65]
+// and s_x[64] are LDS; every thread of the workgroup calls it, and it returns with the
+// workgroup converged (a request outside the row capacity returns early for all).
+constexpr int kFusedPer = 8;    // loads in flight per lane
+// Requests up to which the streaming greedy verify decides inside the contraction's launch.
+constexpr int kGreedyTailMaxRequests = 2;
+
+__device__ inline void merge_accept_greedy_request(
+    const VerifyArgs &a, int r, int n, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ next_token, int64_t *__restrict__ counters, int nw, int *s_arg,
+    int *s_x) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gamma = a.rm.gamma;
+  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  const int cap = a.rm.B * (gamma + 1);
+  const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
+  if (base < 0 || base + L >= cap) {
+    if (tid == 0) {
+      raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      accept_len[r] = 0;
+      next_token[r] = -1;
+    }
+    return;
+  }
+  for (int j = wave; j <= L; j += nw) {
+    const int m = base + j;
+    // The drafted token, its logit from the contraction when that left one, and the
+    // partials are loaded together; only without a logit (NaN or none) are the hidden
+    // and LM-head rows read for the fp64 dot.
+    const int x = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
+    const bool has_x = x >= 0 && x < a.V;
+    double zg = 0.0;
+    if (has_x && a.zx) zg = a.zx[m];
+    const TilePartial *P = a.partials + (size_t)m * a.part_stride;
+    float t1 = -INFINITY, t2 = -INFINITY;
+    int a1 = 0x7fffffff;
+    for (int p0 = 0; p0 < n; p0 += 64 * kFusedPer) {
+      TilePartial q[kFusedPer];
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i) {
+        const int p = p0 + lane + 64 * i;
+        q[i] = p < n ? P[p] : TilePartial{-INFINITY, -INFINITY, 0x7fffffff, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i) {
+        if (beats(q[i].top1, q[i].arg, t1, a1)) { t2 = fmaxf(t1, q[i].top2); t1 = q[i].top1; a1 = q[i].arg; }
+        else { t2 = fmaxf(t2, q[i].top1); }
+      }
+    }
+    const bool need_dot = has_x && (!a.zx || zg != zg);
+    double part = 0.0;
+    if (need_dot)
+      part = lm_head_dot_part(a, a.hidden + ((size_t)r * (gamma + 1) + j) * a.d, x, lane, 64);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+      const int oa = __shfl_xor(a1, off);
+      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+      else { t2 = fmaxf(t2, o1); }
+      part += __shfl_xor(part, off);
+    }
+    if (lane == 0) {
+      sd_row_stats st;
+      st.argmax = a1;
+      st.top1 = t1;
+      st.top2 = t2;
+      st.pos = j;
+      st.lse = 0.0;
+      st.z_draft = need_dot ? part : (has_x ? zg : 0.0);
+      a.stats[m] = st;
+      s_arg[j] = a1;
+      if (j < L) s_x[j] = x;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool miss = lane < L && s_arg[lane] != s_x[lane];
+    const unsigned long long mask = __ballot(miss);
+    const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
+    if (lane == 0) {
+      accept_len[r] = acc;
+      next_token[r] = s_arg[acc];
+      if (counters) {
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)acc);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------- streaming regime, direct to LDS
 // The streaming kernel for d % KC == 0. global_load_lds_dwordx4 moves every wave
 // load's 1 KB (four 256-byte row segments for KC = 128) straight into one of NS LDS
@@ -688,6 +781,26 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     p.top1 = r0.t1; p.top2 = r0.t2; p.arg = r0.arg; p.sum = r0.sum;
     a.partials[(size_t)tid * a.part_stride + g] = p;
   }
+  if (!a.greedy_accept_len) return;
+
+  // Greedy verify tail in this launch (no second kernel). Each workgroup makes its
+  // partials and drafted-token logits visible device-wide, then takes a ticket; the
+  // workgroup that draws the last one merges every request's rows and decides, exactly
+  // as k_merge_accept_greedy does, and returns the ticket counter to zero for the next
+  // launch. No workgroup waits for another.
+  __threadfence();
+  __syncthreads();
+  int *s_i = reinterpret_cast<int *>(S);
+  if (tid == 0) s_i[0] = atomicAdd(&a.ws->ticket, 1u) == (unsigned)(G - 1);
+  __syncthreads();
+  if (!s_i[0]) return;
+  __threadfence();
+  for (int r = 0; r < a.rm.B; ++r) {
+    merge_accept_greedy_request(a, r, G, a.greedy_accept_len, a.greedy_next_token,
+                                a.greedy_counters, 4, s_i + 4, s_i + 72);
+    __syncthreads();   // s_arg and s_x are rewritten by the next request
+  }
+  if (tid == 0) a.ws->ticket = 0u;
 }
 
 // ----------------------------------------------------------------- tiled regime
@@ -1223,94 +1336,15 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
   if (tid == 0) write_stats(a, m, t1, t2, a1, lse, zd);
 }
 
-// Greedy verify tail in one kernel: one workgroup per request merges the partials of
-// its rows 0..L_r (one wave per row), writes their statistics with the drafted
-// token's exact logit, then finds the first row whose argmax differs from the draft
-// and emits that row's argmax (LFM2.5-DSpark blog, "Quality parity").
+// Greedy verify tail in one kernel: one workgroup of kFusedWaves waves per request.
 constexpr int kFusedWaves = 16;
-constexpr int kFusedPer = 8;    // loads in flight per lane
 
 __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
     VerifyArgs a, int n, int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
     int64_t *__restrict__ counters) {
   __shared__ int s_arg[65], s_x[64];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int gamma = a.rm.gamma;
-  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
-  const int cap = a.rm.B * (gamma + 1);
-  const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
-  if (base < 0 || base + L >= cap) {
-    if (tid == 0) {
-      raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
-      accept_len[r] = 0;
-      next_token[r] = -1;
-    }
-    return;
-  }
-  for (int j = wave; j <= L; j += kFusedWaves) {
-    const int m = base + j;
-    // The drafted token, its logit from the contraction when that left one, and the
-    // partials are loaded together; only without a logit (NaN or none) are the hidden
-    // and LM-head rows read for the fp64 dot.
-    const int x = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
-    const bool has_x = x >= 0 && x < a.V;
-    double zg = 0.0;
-    if (has_x && a.zx) zg = a.zx[m];
-    const TilePartial *P = a.partials + (size_t)m * a.part_stride;
-    float t1 = -INFINITY, t2 = -INFINITY;
-    int a1 = 0x7fffffff;
-    for (int p0 = 0; p0 < n; p0 += 64 * kFusedPer) {
-      TilePartial q[kFusedPer];
-#pragma unroll
-      for (int i = 0; i < kFusedPer; ++i) {
-        const int p = p0 + lane + 64 * i;
-        q[i] = p < n ? P[p] : TilePartial{-INFINITY, -INFINITY, 0x7fffffff, 0.f};
-      }
-#pragma unroll
-      for (int i = 0; i < kFusedPer; ++i) {
-        if (beats(q[i].top1, q[i].arg, t1, a1)) { t2 = fmaxf(t1, q[i].top2); t1 = q[i].top1; a1 = q[i].arg; }
-        else { t2 = fmaxf(t2, q[i].top1); }
-      }
-    }
-    const bool need_dot = has_x && (!a.zx || zg != zg);
-    double part = 0.0;
-    if (need_dot)
-      part = lm_head_dot_part(a, a.hidden + ((size_t)r * (gamma + 1) + j) * a.d, x, lane, 64);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-      const int oa = __shfl_xor(a1, off);
-      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-      else { t2 = fmaxf(t2, o1); }
-      part += __shfl_xor(part, off);
-    }
-    if (lane == 0) {
-      sd_row_stats st;
-      st.argmax = a1;
-      st.top1 = t1;
-      st.top2 = t2;
-      st.pos = j;
-      st.lse = 0.0;
-      st.z_draft = need_dot ? part : (has_x ? zg : 0.0);
-      a.stats[m] = st;
-      s_arg[j] = a1;
-      if (j < L) s_x[j] = x;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const bool miss = lane < L && s_arg[lane] != s_x[lane];
-    const unsigned long long mask = __ballot(miss);
-    const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
-    if (lane == 0) {
-      accept_len[r] = acc;
-      next_token[r] = s_arg[acc];
-      if (counters) {
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)acc);
-      }
-    }
-  }
+  merge_accept_greedy_request(a, blockIdx.x, n, accept_len, next_token, counters, kFusedWaves,
+                              s_arg, s_x);
 }
 
 // Resident workgroups per CU of each persistent kernel, cached per host thread for the
@@ -1371,23 +1405,35 @@ int stage_stride(int nst) {
   return 1;
 }
 
+// The greedy tail inside the streaming contraction pays a device-scope release fence
+// per workgroup and merges in one 4-wave workgroup; it beats a separate merge launch only
+// on small grids (measured: a 16-workgroup grid's step 17.5 -> 10.8 us, a 512-workgroup
+// grid's 28 -> 98 us).
+constexpr int kGreedyTailMaxGrid = 32;
+
 template <int MT, int KC, int NS, int FMT>
-hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part,
+                            bool *greedy_done) {
   const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS, FMT>);
   const int G = persistent_grid((a.V + 63) / 64, resident_blocks(fn), a.part_stride);
   *n_part = G;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G), dim3(256), 0, stream, a,
+  VerifyArgs k = a;
+  const bool tail = a.greedy_accept_len && G <= kGreedyTailMaxGrid;
+  if (!tail) k.greedy_accept_len = nullptr;
+  if (greedy_done) *greedy_done = tail;
+  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G), dim3(256), 0, stream, k,
                      stage_stride(a.d / KC));
   return hipGetLastError();
 }
 
 template <int MT, int KC, int NS>
-hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part) {
+hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part,
+                         bool *greedy_done) {
   if constexpr (KC == 128) {
-    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, kLmW12>(a, stream, n_part);
-    if (a.w_blocked) return launch_skinny_as<MT, KC, NS, kLmBlocked>(a, stream, n_part);
+    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, kLmW12>(a, stream, n_part, greedy_done);
+    if (a.w_blocked) return launch_skinny_as<MT, KC, NS, kLmBlocked>(a, stream, n_part, greedy_done);
   }
-  return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part);
+  return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part, greedy_done);
 }
 
 // Blocked copy of a bf16 LM head: block (st, s), stored stage-major at index
@@ -1434,14 +1480,15 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
 }
 
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                              bool *zx_done) {
+                              bool *zx_done, bool *greedy_done) {
   const int cap = a.rm.B * (a.rm.gamma + 1);
   *zx_done = false;
+  if (greedy_done) *greedy_done = false;
   if (a.d % 128 == 0 && cap <= 64) *zx_done = a.zx != nullptr && a.draft_tokens != nullptr;
   if (a.d % 128 == 0) {
-    if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part);
-    if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part);
-    if (cap <= 64) return launch_skinny<4, 128, 2>(a, stream, n_part);
+    if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part, greedy_done);
+    if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part, greedy_done);
+    if (cap <= 64) return launch_skinny<4, 128, 2>(a, stream, n_part, greedy_done);
   }
   if (cap <= 16) return launch_stream<1, 64, 256>(a, stream, n_part);
   if (cap <= 32) return launch_stream<2, 64, 128>(a, stream, n_part);
@@ -1469,10 +1516,18 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
 
 hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
                                 int64_t *counters, hipStream_t stream) {
+  // A small streaming contraction with few requests finishes the step in its own launch
+  // (its last workgroup merges and decides); otherwise a separate launch does that.
+  VerifyArgs f = a;
+  if (a.rm.B <= kGreedyTailMaxRequests && a.zx && a.draft_tokens) {
+    f.greedy_accept_len = accept_len;
+    f.greedy_next_token = next_token;
+    f.greedy_counters = counters;
+  }
   int n_part = 0;
-  bool zx_done = false;
-  hipError_t e = launch_contraction(a, stream, &n_part, &zx_done);
-  if (e != hipSuccess) return e;
+  bool zx_done = false, greedy_done = false;
+  hipError_t e = launch_contraction(f, stream, &n_part, &zx_done, &greedy_done);
+  if (e != hipSuccess || greedy_done) return e;
   VerifyArgs m = a;
   if (!zx_done) m.zx = nullptr;
   hipLaunchKernelGGL(k_merge_accept_greedy, dim3(a.rm.B), dim3(64 * kFusedWaves), 0, stream, m,

@@ -127,6 +127,12 @@ struct VerifyArgs {
   // Blocked bf16 LM head: W holds [d/128][ceil(V/64)][64][128] (stage-major), row r's
   // 16-byte chunk j of a block at position j ^ (r & 15), rows past V zero.
   bool w_blocked;
+  // Greedy verify decided inside the streaming contraction's launch: when
+  // greedy_accept_len is set, its last workgroup writes the statistics and these outputs
+  // (counters may be null). Uses the workspace header's ticket word.
+  int32_t *greedy_accept_len;
+  int32_t *greedy_next_token;
+  int64_t *greedy_counters;
 };
 
 // LM-head formats of the streaming contraction.

@@ -18,9 +18,12 @@ hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
                                 int64_t *counters, hipStream_t stream);
 // The contraction kernel alone; *n_part receives the partial columns written per row and
-// *zx_done whether it also wrote the drafted-token logits to a.zx.
+// *zx_done whether it also wrote the drafted-token logits to a.zx. With
+// a.greedy_accept_len set, *greedy_done (when given) says whether the launch also wrote
+// the greedy statistics and decisions (small streaming grids); otherwise the caller
+// still has to.
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                              bool *zx_done);
+                              bool *zx_done, bool *greedy_done = nullptr);
 
 // Stage-major blocked copy of a bf16 LM head (the layout VerifyArgs::w_blocked reads).
 hipError_t launch_block_lm_head(const uint16_t *W, int V, int d, uint16_t *out,

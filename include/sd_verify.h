@@ -203,8 +203,11 @@ SD_API int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_
  * Greedy verify of a drafted block in one call (LFM2.5-DSpark blog, "How DSpark
  * works" and "Quality parity"): the LM-head contraction at temperature 0 followed
  * by one kernel that merges each request's row statistics and decides acceptance.
+ * When the streaming contraction runs on a grid of at most 32 workgroups for at most
+ * 2 requests, its last workgroup merges and decides instead (no second launch); that
+ * uses the workspace header's ticket word, which every call leaves at zero.
  * Outputs are the same bytes as sd_verify_logits (temperature 0, logits NULL)
- * followed by sd_accept_greedy, with one launch fewer.
+ * followed by sd_accept_greedy, with one or two launches fewer.
  *   hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma, d, V
  *                as for sd_verify_logits (draft_tokens required)
  *   stats        sd_row_stats [B * (gamma + 1)]  out, as for sd_verify_logits

@@ -203,15 +203,25 @@ def test_determinism_bytes():
     ("fused-tiled", dict(B=20, gamma=8, d=128, V=5000, truncate=True)),
     ("fused-gamma64", dict(B=2, gamma=64, d=64, V=700)),
     ("fused-many", dict(B=300, gamma=3, d=64, V=129, truncate=True)),
+    # Streaming grids of at most 32 workgroups with at most 2 requests decide inside the
+    # contraction's launch (its last workgroup merges); 2048 ids = 32 slabs of 64.
+    ("tail-tiny", dict(B=1, gamma=4, d=256, V=1024)),
+    ("tail-32-trunc", dict(B=2, gamma=9, d=384, V=2048, truncate=True)),
+    ("tail-blocked", dict(B=2, gamma=7, d=256, V=1500, blocked=True)),
+    ("tail-33-separate", dict(B=1, gamma=9, d=256, V=2049)),
 ], ids=lambda c: c[0])
 def test_fused_greedy_matches_separate_calls(case):
     """sd_verify_greedy writes the same bytes as sd_verify_logits + sd_accept_greedy."""
     name, over = case
+    over = dict(over)
+    blocked = over.pop("blocked", False)
     base = "greedy-block9" if name == "greedy-block9" else "ragged-b32"
     over = dict(over, T=0.0, name=name) if name != "greedy-block9" else dict(name=name)
     w = workload(base, **over)
     W = make_weights(w)
     W_dev = bf16_dev(W)
+    if blocked:
+        W_dev = sd.BlockedWeights(W_dev)
     for step in range(2):
         ds = upload_step(make_step(w, W, step))
         outs = []

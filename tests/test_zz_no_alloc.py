@@ -62,15 +62,19 @@ def need_gpu():
 
 def test_noalloc_matches_workspace_call_twice_shrinking():
     # Calls in a row, each smaller than the one before: a tiled-regime problem (24
-    # truncated requests), the greedy block of 9 at full size for 4 requests, then a
-    # small truncating one. Partials and drafted-token logits of earlier calls remain in
-    # the scratch and must not leak into later ones.
+    # truncated requests), the greedy block of 9 at full size for 4 requests, a small
+    # truncating one, then a tiny one whose 16-workgroup contraction also decides (its
+    # last workgroup merges, using the scratch header's ticket word). Partials and
+    # drafted-token logits of earlier calls remain in the scratch and must not leak into
+    # later ones.
     tiled = workload("ragged-b32", B=24, gamma=16, d=256, V=20000, T=0.0, name="noalloc-tiled")
     big = workload("greedy-block9", B=4, name="noalloc-big")
     small = workload("ragged-b32", B=3, gamma=16, d=512, V=3001, T=0.0, name="noalloc-small")
-    sizes = [sd.verify_workspace_bytes(w.B, w.gamma, w.d, w.V) for w in (tiled, big, small)]
-    assert sizes[0] > sizes[1] > sizes[2] and sizes[0] <= sd.NOALLOC_SCRATCH_BYTES
-    for w, trunc in ((tiled, True), (big, False), (small, True)):
+    tiny = workload("ragged-b32", B=2, gamma=4, d=256, V=1024, T=0.0, name="noalloc-tiny")
+    ws = (tiled, big, small, tiny)
+    sizes = [sd.verify_workspace_bytes(w.B, w.gamma, w.d, w.V) for w in ws]
+    assert sizes[0] > sizes[1] > sizes[2] > sizes[3] and sizes[0] <= sd.NOALLOC_SCRATCH_BYTES
+    for w, trunc in ((tiled, True), (big, False), (small, True), (tiny, True)):
         say(w.name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} truncate={trunc}")
         acc = run_both(w, 0, trunc)
         say("accept_len", acc.tolist())
