@@ -62,6 +62,9 @@ _SIGS = {
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_accept_rejection_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sd_verify_rejection": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz,
+                                   _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -76,6 +79,7 @@ ROW_STATS_DTYPE = np.dtype([("argmax", "<i4"), ("top1", "<f4"), ("top2", "<f4"),
 assert ROW_STATS_DTYPE.itemsize == 32
 
 FLAG_VERIFY_LEN, FLAG_ROW_OFFSETS, FLAG_NO_RESIDUAL = 1, 2, 4
+LM_HEAD_ROWS, LM_HEAD_BLOCKED = 0, 1
 
 
 class SdError(RuntimeError):
@@ -563,15 +567,79 @@ def _accept_rejection(name, logits, stats, draft_logits, draft_tokens, verify_le
     return accept_len, next_token, accept_rate
 
 
+def sd_verify_rejection(hidden: torch.Tensor, lm_head, draft_tokens: torch.Tensor,
+                        draft_logits: torch.Tensor, verify_len: Optional[torch.Tensor],
+                        row_offsets: Optional[torch.Tensor], u_accept: torch.Tensor,
+                        u_resample: torch.Tensor, temperature: float,
+                        logits: Optional[torch.Tensor] = None,
+                        stats: Optional[torch.Tensor] = None,
+                        accept_len: Optional[torch.Tensor] = None,
+                        next_token: Optional[torch.Tensor] = None,
+                        counters: Optional[torch.Tensor] = None,
+                        accept_rate: Optional[torch.Tensor] = None,
+                        ws_verify: Optional[torch.Tensor] = None,
+                        ws_accept: Optional[torch.Tensor] = None, stream=None):
+    """Rejection verify in one call: returns (logits, stats, accept_len, next_token).
+    lm_head: bf16 [V][d] tensor or BlockedWeights; accept_rate float64 [B][gamma] or None
+    (not computed)."""
+    _need(hidden, "hidden", torch.bfloat16)
+    B, g1, d = hidden.shape
+    g = g1 - 1
+    if isinstance(lm_head, BlockedWeights):
+        if lm_head.d != d:
+            raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
+        head, V, layout = _ptr(lm_head.buf), lm_head.V, LM_HEAD_BLOCKED
+    else:
+        head, V, fmt = _lm_head(lm_head, d)
+        if fmt:
+            raise ValueError("sd_verify_rejection reads a bf16 LM head or its blocked copy")
+        layout = LM_HEAD_ROWS
+    dev = hidden.device
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
+    _need(draft_logits, "draft_logits", torch.bfloat16, (B, g, V))
+    if verify_len is not None:
+        _need(verify_len, "verify_len", torch.int32, (B,))
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    _need(u_accept, "u_accept", torch.float32, (B, g))
+    _need(u_resample, "u_resample", torch.float32, (B, g1))
+    if logits is None:
+        logits = torch.empty((B * g1, V), dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, (B * g1, V))
+    if stats is None:
+        stats = new_stats(B, g, dev)
+    _need(stats, "stats", torch.int64, (B * g1, 4))
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _need(next_token, "next_token", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    if accept_rate is not None:
+        _need(accept_rate, "accept_rate", torch.float64, (B, g))
+    if ws_verify is None:
+        ws_verify = new_workspace(verify_workspace_bytes(B, g, d, V), dev, stream)
+    if ws_accept is None:
+        ws_accept = new_workspace(accept_workspace_bytes(B, g, V), dev, stream)
+    _check("sd_verify_rejection", _lib.sd_verify_rejection(
+        _ptr(hidden), head, layout, _ptr(draft_logits), _ptr(draft_tokens), _ptr(verify_len),
+        _ptr(row_offsets), _ptr(u_accept), _ptr(u_resample), B, g, d, V, float(temperature),
+        _ptr(logits), _ptr(stats), _ptr(accept_len), _ptr(next_token), _ptr(counters),
+        _ptr(accept_rate), _ptr(ws_verify), ws_verify.numel(), _ptr(ws_accept),
+        ws_accept.numel(), _stream(stream)))
+    return logits, stats, accept_len, next_token
+
+
 # --------------------------------------------------------------- a whole round
 
 class VerifyRound:
     """Buffers for repeated verify rounds of one shape; each run() enqueues the whole path.
 
     truncate -> verify logits -> accept (greedy when temperature == 0, else rejection),
-    all on one stream with no host synchronisation. At temperature 0 the verify and
-    accept steps run through sd_verify_greedy (one launch fewer); fused=False keeps
-    the separate sd_verify_logits + sd_accept_greedy calls.
+    all on one stream with no host synchronisation. The verify and accept steps run
+    through sd_verify_greedy at temperature 0 and sd_verify_rejection otherwise (fewer
+    launches; a W12 LM head keeps the separate rejection calls); fused=False keeps the
+    separate sd_verify_logits + sd_accept_* calls.
     """
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
@@ -616,6 +684,12 @@ class VerifyRound:
             sd_verify_greedy(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                              self.stats, self.accept_len, self.next_token, self.counters,
                              self.ws_verify, stream=stream)
+            return self.accept_len, self.next_token
+        if self.T > 0 and self.fused and not isinstance(lm_head, W12Weights):
+            sd_verify_rejection(hidden, lm_head, draft_tokens, draft_logits, self.verify_len,
+                                self.row_offsets, u_accept, u_resample, self.T, self.logits,
+                                self.stats, self.accept_len, self.next_token, self.counters,
+                                self.accept_rate, self.ws_verify, self.ws_accept, stream=stream)
             return self.accept_len, self.next_token
         sd_verify_logits(hidden, lm_head, draft_tokens, self.verify_len, self.row_offsets,
                          self.T, self.logits, self.stats, self.ws_verify, stream=stream)

@@ -13,6 +13,7 @@
 // from p.
 #include <math.h>
 
+#include "sd_draft.h"
 #include "sd_launch.h"
 
 namespace sdv {
@@ -112,14 +113,8 @@ __global__ __launch_bounds__(256) void k_accept_greedy(const sd_row_stats *__res
 //                     max(0, p - q) after a rejection, p for the bonus row;
 //   k_draw_finalize   (request): find the chunk where the running sum crosses
 //                     u_resample * S and scan it for the token.
-constexpr int kChunk = 4096;            // vocabulary ids per chunk
+constexpr int kChunk = kDraftChunk;      // vocabulary ids per chunk
 constexpr int kPer = kChunk / 256;      // ids per thread per chunk
-
-struct DraftPart {
-  float m;       // max drafter logit of the chunk (raw, before / T)
-  float pad;
-  double s;      // sum over the chunk of exp((l - m) / T)
-};
 
 struct RejArgs {
   const float *logits;
@@ -135,18 +130,20 @@ struct RejArgs {
   int32_t *accept_len, *next_token;
   int64_t *counters;
   double *lse_q;             // [B][gamma]
-  int32_t *acc_a;            // [B] accepted length, -1 for a request outside the row capacity
+  DrawRec *rec;              // [B] the draw each request takes
+  float *qx;                 // [B][gamma] drafter logit of each kept row's drafted token
   DraftPart *dpart;          // [B][gamma][C]
   double *csum;              // [B][C][2]: residual (or bonus) weight sum, p weight sum
   double *rate_part;         // [B][gamma][C] acceptance-rate chunk sums, or null
   double *rate;              // [B][gamma] acceptance rate out, or null
   WsHeader *ws;
+  // Drafted-token logits formed beside the drafter normaliser (rejection verify in one
+  // call, when the contraction does not form them): hidden bf16 [B][gamma + 1][d], the
+  // bf16 [V][d] LM head, out zx [B (gamma + 1)] fp64 at the packed rows; zx null otherwise.
+  const uint16_t *hidden, *W;
+  int d;
+  double *zx;
 };
-
-// 2^x by the hardware instruction. It returns no denormals: results below 2^-126 are 0,
-// far below anything the sums and draws here resolve (each draw or sum is relative to a
-// row whose weights add up to 1).
-__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline double block_sum_d(double x, double *red) {
 #pragma unroll
@@ -160,90 +157,52 @@ __device__ inline double block_sum_d(double x, double *red) {
 }
 
 // Drafter-row normaliser, one wave per (chunk, kept draft row): the chunk's 4096 drafter
-// logits arrive as eight 1 KB wave loads (load h gives lane l ids c * kChunk + 512 h + 8 l
-// .. + 7; ids past V count as -inf), and the chunk's max and sum are reduced with lane
-// exchanges only, with no workgroup barrier. Rows are 16-byte aligned when V % 8 == 0;
-// otherwise the chunk is read one id at a time (two passes).
+// logits arrive as eight 1 KB wave loads and the chunk's max and sum are reduced with lane
+// exchanges only, with no workgroup barrier (draft_chunk_partial).
 constexpr int kDraftWaves = 4;
 
-__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Loads of chunk c of an aligned row (V % 8 == 0, so V >= 8 and v0 < V means v0 + 8 <= V).
-// The address is clamped into the row, so every lane loads; past V the value is -inf.
-__device__ inline void draft_chunk_load(const uint16_t *row, int V, int c, int lane, u32x4 (&w)[8]) {
+// Drafted-token logit of every kept draft row (the workgroup of grid column x = last when
+// a.zx is set; grid y strides over the rows): the exact fp64 dot of the bf16 hidden and
+// LM-head rows, chunk c of d/8 taken by thread c % 256 (four held, the rest in a loop),
+// then a fixed-order workgroup sum -- the arithmetic of the verify call's row merge, so
+// the value is the same bits. Rows with an out-of-range token or outside the row
+// capacity are left alone (the decision treats them itself).
+__device__ void draft_token_logits(const RejArgs &a, double *red) {
+  const int gamma = a.rm.gamma, tid = threadIdx.x, nc = a.d / 8;
+  for (int rj = blockIdx.y; rj < a.rm.B * gamma; rj += gridDim.y) {
+    const int r = rj / gamma, j = rj - r * gamma;
+    const int L = clamp_len(a.verify_len, r, gamma, nullptr);
+    if (j >= L) continue;
+    const int base = request_base(a.rm, r, L, nullptr);
+    const int x = a.draft_tokens[rj];
+    if (base < 0 || x < 0 || x >= a.V) continue;
+    const uint16_t *h = a.hidden + ((size_t)r * (gamma + 1) + j) * a.d;
+    const uint16_t *w = a.W + (size_t)x * a.d;
+    u32x4 hv[4], wv[4];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    const int v0 = c * kChunk + 512 * h + 8 * lane;
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + min(v0, V - 8)));
-    const u32x4 ninf{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // bf16 -inf
-    w[h] = v0 < V ? x : ninf;
-  }
-}
-
-// Ids at -inf add exp2(-inf) = 0; a chunk that is -inf throughout sums to 0.
-__device__ inline DraftPart draft_part(float m, const float (&sh)[8]) {
-  double S = 0.0;
-  if (m != -INFINITY) {
-#pragma unroll
-    for (int h = 0; h < 8; ++h) S += (double)sh[h];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-  }
-  DraftPart p;
-  p.m = m; p.pad = 0.f; p.s = S;
-  return p;
-}
-
-__device__ inline DraftPart draft_chunk_stats(const u32x4 (&w)[8], float sl) {
-  float m = -INFINITY;
-#pragma unroll
-  for (int h = 0; h < 8; ++h)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(bf_lo(w[h][q]), bf_hi(w[h][q])));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float sh[8];
-#pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    sh[h] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sh[h] += exp2_hw((bf_lo(w[h][q]) - m) * sl);
-      sh[h] += exp2_hw((bf_hi(w[h][q]) - m) * sl);
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      hv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(h + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      wv[i] = c < nc ? *reinterpret_cast<const u32x4 *>(w + 8 * c) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  return draft_part(m, sh);
-}
-
-__device__ inline DraftPart draft_chunk_unaligned(const uint16_t *row, int V, int c, int lane,
-                                                  float sl) {
-  float m = -INFINITY;
-#pragma unroll 1
-  for (int h = 0; h < 8; ++h)
-#pragma unroll 1
-    for (int e = 0; e < 8; ++e) {
-      const int v = c * kChunk + 512 * h + 8 * lane + e;
-      if (v < V) m = fmaxf(m, bf16_to_f32(row[v]));
-    }
+    double part = 0.0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float sh[8];
-#pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    sh[h] = 0.f;
-#pragma unroll 1
-    for (int e = 0; e < 8; ++e) {
-      const int v = c * kChunk + 512 * h + 8 * lane + e;
-      if (v < V) sh[h] += exp2_hw((bf16_to_f32(row[v]) - m) * sl);
-    }
+    for (int i = 0; i < 4; ++i) part += dot8_f64(hv[i], wv[i]);
+    for (int c = tid + 1024; c < nc; c += 256)
+      part += dot8_f64(*reinterpret_cast<const u32x4 *>(h + 8 * c), *reinterpret_cast<const u32x4 *>(w + 8 * c));
+    part = block_sum_d(part, red);
+    if (tid == 0) a.zx[base + j] = part;
   }
-  return draft_part(m, sh);
 }
 
 // Full grid: a workgroup's waves take neighbouring chunks of one row; grid y strides over
-// the rows.
+// the rows. With a.zx set, the last grid column forms the drafted-token logits instead.
 __global__ __launch_bounds__(64 * kDraftWaves) void k_draft_partial(RejArgs a) {
+  __shared__ double red[4];
+  if (a.zx && blockIdx.x == gridDim.x - 1) {
+    draft_token_logits(a, red);
+    return;
+  }
   const int gamma = a.rm.gamma, lane = threadIdx.x & 63;
   const int c = blockIdx.x * kDraftWaves + (threadIdx.x >> 6);
   if (c >= a.C) return;
@@ -253,33 +212,38 @@ __global__ __launch_bounds__(64 * kDraftWaves) void k_draft_partial(RejArgs a) {
     const int L = clamp_len(a.verify_len, r, gamma, c == 0 && lane == 0 ? a.ws : nullptr);
     if (j >= L) continue;
     const uint16_t *row = a.draft_logits + (size_t)rj * V;
-    DraftPart p;
-    if ((V & 7) == 0) {
-      u32x4 w[8];
-      draft_chunk_load(row, V, c, lane, w);
-      p = draft_chunk_stats(w, a.sl);
-    } else {
-      p = draft_chunk_unaligned(row, V, c, lane, a.sl);
+    const int x = a.draft_tokens[rj];
+    const bool own_x = x >= 0 && x < V && x / kChunk == c;
+    const float lx = own_x ? bf16_to_f32(row[x]) : 0.f;
+    const DraftPart p = draft_chunk_partial(row, V, c, lane, a.sl);
+    if (lane == 0) {
+      a.dpart[(size_t)rj * a.C + c] = p;
+      if (own_x) a.qx[rj] = lx;
     }
-    if (lane == 0) a.dpart[(size_t)rj * a.C + c] = p;
   }
 }
 
-// One workgroup per request; 16 lanes per draft row (16 rows per pass). A row's
-// token, statistics, uniform and chunk partials are loaded together, the drafted
-// token's drafter logit as soon as its id is known.
+// One workgroup per request; 16 lanes per draft row (16 rows per pass). A row's token,
+// statistics, uniform, chunk partials and the drafter logit of its token (left by the
+// drafter normaliser) are loaded together. The request's draw record follows a_r.
 constexpr int kDecideHold = 4;   // chunk partials held per lane (C <= 64 without reloads)
 
 __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
   __shared__ int s_rej[64];
+  __shared__ double s_lse[65], s_lseq[64];
   const int r = blockIdx.x, tid = threadIdx.x, sub = tid & 15;
   const int gamma = a.rm.gamma;
   const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
   const int base = request_base(a.rm, r, L, tid == 0 ? a.ws : nullptr);
   if (base < 0) {
-    if (tid == 0) { a.acc_a[r] = -1; a.accept_len[r] = 0; a.next_token[r] = -1; }
+    if (tid == 0) {
+      a.rec[r] = draw_record(-1, 0, 0, -1, 0.0, 0.0, a.invT);
+      a.accept_len[r] = 0;
+      a.next_token[r] = -1;
+    }
     return;
   }
+  if (tid == 0) s_lse[L] = a.stats[base + L].lse;   // the bonus row
   for (int j0 = 0; j0 < L; j0 += 16) {
     const int j = j0 + (tid >> 4);
     const bool live = j < L;
@@ -300,7 +264,7 @@ __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
       const int c = sub + 16 * i;
       hold[i] = live && c < a.C ? P[c] : DraftPart{-INFINITY, 0.f, 0.0};
     }
-    const float lx = xok ? bf16_to_f32(a.draft_logits[rj * a.V + x]) : 0.f;
+    const float lx = xok ? a.qx[rj] : 0.f;
     float M = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kDecideHold; ++i) M = fmaxf(M, hold[i].m);
@@ -310,16 +274,18 @@ __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
     double S = 0.0;
 #pragma unroll
     for (int i = 0; i < kDecideHold; ++i)
-      if (hold[i].s != 0.0) S += hold[i].s * exp(((double)hold[i].m - (double)M) * a.invT);
+      if (hold[i].s != 0.0) S += hold[i].s * partial_weight(hold[i].m, M, a.sl);
     for (int c = sub + 16 * kDecideHold; live && c < a.C; c += 16) {
       const DraftPart q = P[c];
-      if (q.s != 0.0) S += q.s * exp(((double)q.m - (double)M) * a.invT);
+      if (q.s != 0.0) S += q.s * partial_weight(q.m, M, a.sl);
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) S += __shfl_xor(S, off);
     if (live && sub == 0) {
       const double lse = (double)M * a.invT + log(S);
       a.lse_q[rj] = lse;
+      s_lse[j] = lse_p;
+      s_lseq[j] = lse;
       int rej = 1;
       if (xok) {
         const double logp = zx * a.invT - lse_p;
@@ -334,7 +300,7 @@ __global__ __launch_bounds__(256) void k_accept_decide(RejArgs a) {
     const unsigned long long m = __ballot(tid < L && s_rej[tid]);
     if (tid == 0) {
       const int acc = m ? (__ffsll((long long)m) - 1) : L;
-      a.acc_a[r] = acc;
+      a.rec[r] = draw_record(base, acc, L, r * gamma + acc, s_lse[acc], s_lseq[acc], a.invT);
       a.accept_len[r] = acc;
       if (a.counters) {
         atomicAdd(reinterpret_cast<unsigned long long *>(a.counters), (unsigned long long)L);
@@ -365,21 +331,16 @@ struct DrawRow {
   ProbScale ps, qs;      // p and q of the row
 };
 
-__device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow) {
-  const int acc = a.acc_a[r];
-  if (acc < 0) return false;
-  const int gamma = a.rm.gamma;
-  const int L = clamp_len(a.verify_len, r, gamma, nullptr);
-  const int base = request_base(a.rm, r, L, nullptr);
-  d->z = a.logits + (size_t)(base + acc) * a.V;
-  d->ps = prob_scale(a.stats[base + acc].lse, a);
-  d->q = nullptr;
-  d->qs = prob_scale(0.0, a);
-  if (acc < L) {
-    d->q = a.draft_logits + ((size_t)r * gamma + acc) * a.V;
-    d->qs = prob_scale(a.lse_q[(size_t)r * gamma + acc], a);
-  }
-  *arow = base + acc;
+// The draw of request r from its record: false for a request outside the row capacity.
+__device__ inline bool draw_row(const RejArgs &a, int r, DrawRow *d, int *arow, int *acc) {
+  const DrawRec rec = a.rec[r];
+  if (rec.row < 0) return false;
+  d->z = a.logits + (size_t)rec.row * a.V;
+  d->ps = ProbScale{rec.cp, a.sl};
+  d->q = rec.qrow >= 0 ? a.draft_logits + (size_t)rec.qrow * a.V : nullptr;
+  d->qs = ProbScale{rec.cq, a.sl};
+  *arow = rec.row;
+  *acc = rec.acc;
   return true;
 }
 
@@ -462,8 +423,8 @@ __device__ void rate_finalize(const RejArgs &a, int r) {
 // compute acceptance-rate chunk sums of draft row (row - B).
 __device__ void draw_chunk(const RejArgs &a, int r, int c, double *red) {
   DrawRow d;
-  int arow;
-  if (!draw_row(a, r, &d, &arow)) return;
+  int arow, acc;
+  if (!draw_row(a, r, &d, &arow, &acc)) return;
   double sr = 0.0, sp = 0.0;
 #pragma unroll
   for (int e = 0; e < kPer / 4; ++e) {
@@ -520,10 +481,9 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.rate) rate_finalize(a, r);
   DrawRow d;
-  int arow;
-  if (!draw_row(a, r, &d, &arow)) return;
+  int arow, acc;
+  if (!draw_row(a, r, &d, &arow, &acc)) return;
   const int gamma = a.rm.gamma;
-  const int acc = a.acc_a[r];
   const double *cs = a.csum + (size_t)r * a.C * 2;
   // Chunk sums in chunk order: thread t owns chunks t*K .. t*K + K - 1 (K = ceil(C/256)),
   // an inclusive block scan gives every chunk's running sum.
@@ -691,8 +651,9 @@ size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay) {
   AcceptLayout l;
   l.chunks = C;
   l.lse_q = sizeof(WsHeader);
-  l.acc_a = align_up(l.lse_q + (size_t)B * gamma * sizeof(double), 256);
-  l.dpart = align_up(l.acc_a + (size_t)B * sizeof(int32_t), 256);
+  l.rec = align_up(l.lse_q + (size_t)B * gamma * sizeof(double), 256);
+  l.qx = align_up(l.rec + (size_t)B * sizeof(DrawRec), 256);
+  l.dpart = align_up(l.qx + (size_t)B * gamma * sizeof(float), 256);
   l.csum = align_up(l.dpart + (size_t)B * gamma * C * sizeof(DraftPart), 256);
   const size_t total = align_up(l.csum + (size_t)B * C * 2 * sizeof(double), 256);
   if (lay) *lay = l;
@@ -716,11 +677,35 @@ RejArgs rej_args(const uint16_t *draft_logits, const int32_t *verify_len, const 
   a.sl = (float)(kLog2e / (double)temperature);
   a.invT = 1.0 / (double)temperature;
   a.lse_q = reinterpret_cast<double *>(w + l.lse_q);
-  a.acc_a = reinterpret_cast<int32_t *>(w + l.acc_a);
+  a.rec = reinterpret_cast<DrawRec *>(w + l.rec);
+  a.qx = reinterpret_cast<float *>(w + l.qx);
   a.dpart = reinterpret_cast<DraftPart *>(w + l.dpart);
   a.csum = reinterpret_cast<double *>(w + l.csum);
   a.ws = reinterpret_cast<WsHeader *>(workspace);
   return a;
+}
+
+}  // namespace
+
+namespace {
+
+// The draw launches shared by both rejection paths (a.rec, a.lse_q and the row
+// statistics are written by then).
+hipError_t launch_draws(const RejArgs &a, hipStream_t stream) {
+  const int draw_rows = a.rm.B + (a.rate ? a.rm.B * a.rm.gamma : 0);
+  hipLaunchKernelGGL(k_draw_partial, dim3(a.C, grid_rows(draw_rows)), dim3(256), 0, stream, a,
+                     draw_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_draw_finalize, dim3(a.rm.B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_partial(const RejArgs &a, hipStream_t stream) {
+  const unsigned cols = (a.C + kDraftWaves - 1) / kDraftWaves + (a.zx ? 1 : 0);
+  hipLaunchKernelGGL(k_draft_partial, dim3(cols, grid_rows(a.rm.B * a.rm.gamma)),
+                     dim3(64 * kDraftWaves), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -745,19 +730,58 @@ hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stat
   // ([B][gamma][C] entries of 16 bytes) holds the rate chunk sums.
   a.rate_part = accept_rate ? reinterpret_cast<double *>(a.dpart) : nullptr;
   a.rate = accept_rate;
-  hipError_t e;
-  hipLaunchKernelGGL(k_draft_partial,
-                     dim3((a.C + kDraftWaves - 1) / kDraftWaves, grid_rows(rm.B * rm.gamma)),
-                     dim3(64 * kDraftWaves), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = launch_draft_partial(a, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_accept_decide, dim3(rm.B), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int draw_rows = rm.B + (accept_rate ? rm.B * rm.gamma : 0);
-  hipLaunchKernelGGL(k_draw_partial, dim3(a.C, grid_rows(draw_rows)), dim3(256), 0, stream, a,
-                     draw_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_draw_finalize, dim3(rm.B), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_draws(a, stream);
+}
+
+hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const float *u_resample,
+                                   int32_t *accept_len, int32_t *next_token, int64_t *counters,
+                                   double *accept_rate, void *accept_workspace,
+                                   hipStream_t stream) {
+  RejArgs a = rej_args(v.draft_logits, v.verify_len, v.rm, v.V, v.temperature, accept_workspace);
+  a.logits = v.logits;
+  a.stats = v.stats;
+  a.draft_tokens = v.draft_tokens;
+  a.u_accept = u_accept;
+  a.u_resample = u_resample;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.counters = counters;
+  a.rate_part = accept_rate ? reinterpret_cast<double *>(a.dpart) : nullptr;
+  a.rate = accept_rate;
+  // A streaming contraction normalises the drafter rows in workgroups of its own launch
+  // and forms the drafted-token logits; otherwise one drafter-normaliser launch does both
+  // (the logits only for k_merge_decide: the row merge of larger gamma forms its own).
+  v.dpart = a.dpart;
+  v.qx = a.qx;
+  v.dchunks = a.C;
+  int n_part = 0;
+  bool zx_done = false, draft_done = false;
+  hipError_t e = launch_contraction(v, stream, &n_part, &zx_done, nullptr, &draft_done);
+  if (e != hipSuccess) return e;
+  const bool one_pass = v.rm.gamma <= kDecideMaxGamma;
+  if (!one_pass && (e = launch_row_merge(v, n_part, zx_done, stream)) != hipSuccess) return e;
+  if (!draft_done || (one_pass && !zx_done)) {
+    if (one_pass && !zx_done) {
+      a.hidden = v.hidden;
+      a.W = v.W;
+      a.d = v.d;
+      a.zx = v.zx;
+    }
+    if ((e = launch_draft_partial(a, stream)) != hipSuccess) return e;
+  }
+  if (one_pass) {
+    DecideArgs o{u_accept, a.lse_q, a.rec, accept_len, next_token, counters};
+    e = launch_merge_decide(v, o, n_part, stream);
+  } else {
+    hipLaunchKernelGGL(k_accept_decide, dim3(v.rm.B), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  return launch_draws(a, stream);
 }
 
 }  // namespace sdv

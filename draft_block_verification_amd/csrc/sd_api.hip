@@ -492,4 +492,38 @@ int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
 }
 
 
+int32_t sd_verify_rejection(const uint16_t *hidden, const uint16_t *lm_head,
+                            int32_t lm_head_layout, const uint16_t *draft_logits,
+                            const int32_t *draft_tokens, const int32_t *verify_len,
+                            const int32_t *row_offsets, const float *u_accept,
+                            const float *u_resample, int32_t B, int32_t gamma, int32_t d,
+                            int32_t V, float temperature, float *logits, sd_row_stats *stats,
+                            int32_t *accept_len, int32_t *next_token, int64_t *counters,
+                            double *accept_rate, void *verify_workspace,
+                            size_t verify_workspace_bytes, void *accept_workspace,
+                            size_t accept_workspace_bytes, void *stream) {
+  if (lm_head_layout != SD_LM_HEAD_ROWS && lm_head_layout != SD_LM_HEAD_BLOCKED) return SD_EINVAL;
+  if (!logits || !stats || !draft_logits || !draft_tokens || !u_accept || !u_resample ||
+      !accept_len || !next_token)
+    return SD_EINVAL;
+  if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
+  VerifyArgs a;
+  const int32_t st = verify_setup(hidden, lm_head, nullptr, lm_head_layout == SD_LM_HEAD_BLOCKED,
+                                  draft_tokens, verify_len, row_offsets, B, gamma, d, V,
+                                  temperature, logits, stats, true, verify_workspace,
+                                  verify_workspace_bytes, &a);
+  if (st != SD_OK) return st;
+  if (!aligned(draft_logits, 16) || !aligned(u_accept, 4) || !aligned(u_resample, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||
+      (accept_rate && !aligned(accept_rate, 8)))
+    return SD_EALIGN;
+  if (!accept_workspace || accept_workspace_bytes < accept_ws_bytes(B, gamma, V))
+    return SD_EWORKSPACE;
+  if (!aligned(accept_workspace, 256)) return SD_EALIGN;
+  a.draft_logits = draft_logits;
+  return launch_status(launch_verify_rejection(a, u_accept, u_resample, accept_len, next_token,
+                                               counters, accept_rate, accept_workspace,
+                                               (hipStream_t)stream));
+}
+
 }  // extern "C"

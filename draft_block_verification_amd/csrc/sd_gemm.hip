@@ -21,6 +21,7 @@
 // drafted token's logit is recomputed exactly as an fp64 dot of the bf16 inputs.
 #include <math.h>
 
+#include "sd_draft.h"
 #include "sd_launch.h"
 
 #define LDSP __attribute__((address_space(3)))
@@ -323,17 +324,6 @@ __device__ inline size_t w12_group_offset(int x, int c, int nst) {
   return ((((size_t)(x >> 6) * nst + (c >> 4)) * 64 + (x & 63)) * 16 + (c & 15)) * 12;
 }
 
-// fp64 sum of h[k] * w[k] over eight bf16 pairs.
-__device__ inline double dot8_f64(const u32x4 &hv, const u32x4 &wv) {
-  double part = 0.0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    part += (double)__uint_as_float(hv[e] << 16) * (double)__uint_as_float(wv[e] << 16);
-    part += (double)__uint_as_float(hv[e] & 0xffff0000u) * (double)__uint_as_float(wv[e] & 0xffff0000u);
-  }
-  return part;
-}
-
 // Part of the exact logit hidden . W[x] taken by thread t of nt: groups t, t + nt, ...
 // of the LM-head row (bf16, or W12 codes plus that row's corrections).
 __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h, int x, int t,
@@ -468,6 +458,30 @@ __device__ inline void merge_accept_greedy_request(
   }
 }
 
+// Drafter chunk partials of every kept draft row, walked by the nw workgroups appended to
+// the streaming contraction's grid (this one is number w): wave i of the walk takes items
+// i, i + 4 nw, ... of the (draft row, chunk) list, so neighbouring waves read neighbouring
+// chunks of one row. The bytes are those the standalone drafter-normaliser kernel writes.
+__device__ void draft_partials_walk(const VerifyArgs &a, int w, int nw) {
+  const int lane = threadIdx.x & 63, gamma = a.rm.gamma, C = a.dchunks;
+  const int items = a.rm.B * gamma * C;
+  for (int it = 4 * w + (threadIdx.x >> 6); it < items; it += 4 * nw) {
+    const int rj = it / C, c = it - rj * C;
+    const int r = rj / gamma, j = rj - r * gamma;
+    const int L = clamp_len(a.verify_len, r, gamma, c == 0 && lane == 0 ? a.ws : nullptr);
+    if (j >= L) continue;
+    const uint16_t *row = a.draft_logits + (size_t)rj * a.V;
+    const int x = a.draft_tokens[rj];
+    const bool own_x = x >= 0 && x < a.V && x / kDraftChunk == c;
+    const float lx = own_x ? bf16_to_f32(row[x]) : 0.f;
+    const DraftPart p = draft_chunk_partial(row, a.V, c, lane, a.scale_log2);
+    if (lane == 0) {
+      a.dpart[(size_t)rj * C + c] = p;
+      if (own_x) a.qx[rj] = lx;
+    }
+  }
+}
+
 // ------------------------------------------------- streaming regime, direct to LDS
 // The streaming kernel for d % KC == 0. global_load_lds_dwordx4 moves every wave
 // load's 1 KB (four 256-byte row segments for KC = 128) straight into one of NS LDS
@@ -511,8 +525,14 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
   static_assert(PEND < 64, "vmcnt holds 6 bits");
   __shared__ __attribute__((aligned(16))) uint16_t S[NS * STAGE];
 
+  // Workgroups past the contraction's grid normalise drafter rows instead (rejection
+  // verify in one call); they share no data with the contraction's workgroups.
+  if (a.dpart && (int)blockIdx.x >= a.g_main) {
+    draft_partials_walk(a, (int)blockIdx.x - a.g_main, (int)gridDim.x - a.g_main);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = gridDim.x, g = blockIdx.x;
+  const int G = a.g_main, g = blockIdx.x;
   const int M = rows_total(a.rm);
   const int d = a.d, V = a.V;
 
@@ -1310,11 +1330,11 @@ __global__ __launch_bounds__(256) void k_row_merge(VerifyArgs a, int n) {
     if (n <= 256 * kMergePer) {               // this thread's partials are still in q
 #pragma unroll
       for (int i = 0; i < kMergePer; ++i)
-        if (q[i].sum != 0.f) S += (double)q[i].sum * exp(((double)q[i].top1 - (double)t1) * a.invT);
+        if (q[i].sum != 0.f) S += (double)q[i].sum * partial_weight(q[i].top1, t1, a.scale_log2);
     } else {
       for (int p = tid; p < n; p += 256) {
         const TilePartial o = P[p];
-        if (o.sum != 0.f) S += (double)o.sum * exp(((double)o.top1 - (double)t1) * a.invT);
+        if (o.sum != 0.f) S += (double)o.sum * partial_weight(o.top1, t1, a.scale_log2);
       }
     }
     S = block_sum(S, red);
@@ -1345,6 +1365,157 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_merge_accept_greedy(
   __shared__ int s_arg[65], s_x[64];
   merge_accept_greedy_request(a, blockIdx.x, n, accept_len, next_token, counters, kFusedWaves,
                               s_arg, s_x);
+}
+
+// Rejection verify's row merge and decision in one kernel (DSpark summary, "Problem
+// definition": a draft survives iff u < min(1, p(x) / q(x)), and the first failure ends
+// the accepted prefix). One workgroup of sixteen waves per request, 32 lanes per verified
+// row, so requests of up to 32 rows (gamma <= kDecideMaxGamma), each lane holding sixteen
+// partials in registers. A row's target partials are merged into its
+// statistics -- argmax, top-2 and log sum exp(z / T) -- and written with the drafted
+// token's exact logit; a kept draft row also merges its drafter chunk partials into
+// log sum exp(l / T) and takes the acceptance test. A ballot over the rows gives a_r, and
+// the request's draw record names the row the draw samples. The loads that do not need
+// the request's offset go out first, the partials and drafted-token logits with it.
+// Larger gamma takes the separate row merge and decision kernels.
+constexpr int kDecideLanes = 32;
+constexpr int kDecideHold = 16;   // target partials held per lane (n <= 512 in one round)
+constexpr int kDecideThreads = 1024;
+static_assert(kDecideMaxGamma + 1 == kDecideThreads / kDecideLanes, "one row slot per row");
+
+__global__ __launch_bounds__(kDecideThreads) void k_merge_decide(VerifyArgs a, DecideArgs o, int n) {
+  __shared__ int s_rej[64];
+  __shared__ double s_lse[kDecideMaxGamma + 1], s_lseq[kDecideMaxGamma + 1];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int sub = tid & (kDecideLanes - 1), j = tid / kDecideLanes;   // row slot j
+  const int gamma = a.rm.gamma, V = a.V, C = a.dchunks;
+  // First round of loads: the request's length and offset, and everything of row j that
+  // does not depend on them (its drafted token, uniform and drafter partials; rows past
+  // the length are loaded and then ignored).
+  const size_t rj = (size_t)r * gamma + min(j, gamma - 1);
+  const int xl = a.draft_tokens[rj];
+  const float u = o.u_accept[rj];
+  const float lx = a.qx[rj];   // drafter logit of the token, left by the drafter normaliser
+  DraftPart dq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dq[i] = a.dpart[rj * C + min(sub + kDecideLanes * i, C - 1)];
+  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  const int cap = a.rm.B * (gamma + 1);
+  const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
+  if (base < 0 || base + L >= cap) {
+    if (tid == 0) {
+      raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      o.rec[r] = draw_record(-1, 0, 0, -1, 0.0, 0.0, a.invT);
+      o.accept_len[r] = 0;
+      o.next_token[r] = -1;
+    }
+    return;
+  }
+  if (j <= L) {
+    const int m = base + j;
+    const bool drafted = j < L;
+    const int x = drafted ? xl : -1;
+    const bool has_x = x >= 0 && x < V;
+    // Second round: the row's partials and drafted-token logit (they need the offset).
+    const TilePartial *P = a.partials + (size_t)m * a.part_stride;
+    TilePartial q[kDecideHold];
+#pragma unroll
+    for (int i = 0; i < kDecideHold; ++i) q[i] = P[min(sub + kDecideLanes * i, n - 1)];
+    const double zg = a.zx[m];
+    float t1 = -INFINITY, t2 = -INFINITY;
+    int a1 = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kDecideHold; ++i) {
+      if (sub + kDecideLanes * i >= n) q[i] = TilePartial{-INFINITY, -INFINITY, 0x7fffffff, 0.f};
+      if (beats(q[i].top1, q[i].arg, t1, a1)) { t2 = fmaxf(t1, q[i].top2); t1 = q[i].top1; a1 = q[i].arg; }
+      else { t2 = fmaxf(t2, q[i].top1); }
+    }
+    for (int p = sub + kDecideLanes * kDecideHold; p < n; p += kDecideLanes) {
+      const TilePartial e = P[p];
+      if (beats(e.top1, e.arg, t1, a1)) { t2 = fmaxf(t1, e.top2); t1 = e.top1; a1 = e.arg; }
+      else { t2 = fmaxf(t2, e.top1); }
+    }
+#pragma unroll
+    for (int off = kDecideLanes / 2; off >= 1; off >>= 1) {
+      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+      const int oa = __shfl_xor(a1, off);
+      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+      else { t2 = fmaxf(t2, o1); }
+    }
+    double S = 0.0;
+#pragma unroll
+    for (int i = 0; i < kDecideHold; ++i)
+      if (q[i].sum != 0.f) S += (double)q[i].sum * partial_weight(q[i].top1, t1, a.scale_log2);
+    for (int p = sub + kDecideLanes * kDecideHold; p < n; p += kDecideLanes) {
+      const TilePartial e = P[p];
+      if (e.sum != 0.f) S += (double)e.sum * partial_weight(e.top1, t1, a.scale_log2);
+    }
+    // The drafted token's logit comes from the contraction or the drafter-normaliser
+    // launch; NaN marks a row neither formed (a crowded slab), whose dot is taken here.
+    const bool need_dot = has_x && zg != zg;
+    double part = 0.0;
+    if (need_dot)
+      part = lm_head_dot_part(a, a.hidden + ((size_t)r * (gamma + 1) + j) * a.d, x, sub, kDecideLanes);
+    const DraftPart *Q = a.dpart + rj * C;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (!drafted || sub + kDecideLanes * i >= C) dq[i] = DraftPart{-INFINITY, 0.f, 0.0};
+    float qm = fmaxf(dq[0].m, dq[1].m);
+    for (int c = sub + 2 * kDecideLanes; drafted && c < C; c += kDecideLanes) qm = fmaxf(qm, Q[c].m);
+#pragma unroll
+    for (int off = kDecideLanes / 2; off >= 1; off >>= 1) {
+      S += __shfl_xor(S, off);
+      part += __shfl_xor(part, off);
+      qm = fmaxf(qm, __shfl_xor(qm, off));
+    }
+    double qs = 0.0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (dq[i].s != 0.0) qs += dq[i].s * partial_weight(dq[i].m, qm, a.scale_log2);
+    for (int c = sub + 2 * kDecideLanes; drafted && c < C; c += kDecideLanes) {
+      const DraftPart e = Q[c];
+      if (e.s != 0.0) qs += e.s * partial_weight(e.m, qm, a.scale_log2);
+    }
+#pragma unroll
+    for (int off = kDecideLanes / 2; off >= 1; off >>= 1) qs += __shfl_xor(qs, off);
+    if (sub == 0) {
+      const double lse = (double)t1 * a.invT + log(S);
+      s_lse[j] = lse;
+      sd_row_stats st;
+      st.argmax = a1;
+      st.top1 = t1;
+      st.top2 = t2;
+      st.pos = j;
+      st.lse = lse;
+      st.z_draft = has_x ? (need_dot ? part : zg) : 0.0;
+      a.stats[m] = st;
+      if (drafted) {
+        const double lse_q = (double)qm * a.invT + log(qs);
+        o.lse_q[rj] = lse_q;
+        s_lseq[j] = lse_q;
+        int rej = 1;
+        if (has_x) {
+          const double logp = st.z_draft * a.invT - lse;
+          const double logq = (double)lx * a.invT - lse_q;
+          rej = !((double)u < fmin(1.0, exp(logp - logq)));
+        }
+        s_rej[j] = rej;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const unsigned long long mk = __ballot(tid < L && s_rej[tid]);
+    if (tid == 0) {
+      const int acc = mk ? (__ffsll((long long)mk) - 1) : L;
+      o.rec[r] = draw_record(base, acc, L, r * gamma + acc, s_lse[acc], s_lseq[acc], a.invT);
+      o.accept_len[r] = acc;
+      if (o.counters) {
+        atomicAdd(reinterpret_cast<unsigned long long *>(o.counters), (unsigned long long)L);
+        atomicAdd(reinterpret_cast<unsigned long long *>(o.counters + 1), (unsigned long long)acc);
+      }
+    }
+  }
 }
 
 // Resident workgroups per CU of each persistent kernel, cached per host thread for the
@@ -1411,29 +1582,49 @@ int stage_stride(int nst) {
 // grid's 28 -> 98 us).
 constexpr int kGreedyTailMaxGrid = 32;
 
+// Drafter-normaliser workgroups appended to a streaming contraction of G workgroups out of
+// `resident` slots: the idle slots, up to one workgroup per four (row, chunk) items, and
+// none unless every wave then takes at most kDraftItemsPerWave items (otherwise the
+// walk would run long past the contraction and a separate launch does the work).
+constexpr int kDraftItemsPerWave = 16;
+
+int appended_draft_grid(const VerifyArgs &a, int G, int resident) {
+  const long long items = (long long)a.rm.B * a.rm.gamma * a.dchunks;
+  const int spare = resident - G;
+  if (spare < 1 || items > 4LL * kDraftItemsPerWave * spare) return 0;
+  return (int)min((long long)spare, (items + 3) / 4);
+}
+
 template <int MT, int KC, int NS, int FMT>
 hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                            bool *greedy_done) {
+                            bool *greedy_done, bool *draft_done) {
   const void *fn = reinterpret_cast<const void *>(&k_gemm_skinny<MT, KC, NS, FMT>);
-  const int G = persistent_grid((a.V + 63) / 64, resident_blocks(fn), a.part_stride);
+  const int resident = resident_blocks(fn);
+  const int G = persistent_grid((a.V + 63) / 64, resident, a.part_stride);
   *n_part = G;
   VerifyArgs k = a;
+  k.g_main = G;
   const bool tail = a.greedy_accept_len && G <= kGreedyTailMaxGrid;
   if (!tail) k.greedy_accept_len = nullptr;
   if (greedy_done) *greedy_done = tail;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G), dim3(256), 0, stream, k,
+  const int extra = a.dpart && a.draft_logits ? appended_draft_grid(a, G, resident) : 0;
+  if (!extra) k.dpart = nullptr;
+  if (draft_done) *draft_done = extra > 0;
+  hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G + extra), dim3(256), 0, stream, k,
                      stage_stride(a.d / KC));
   return hipGetLastError();
 }
 
 template <int MT, int KC, int NS>
 hipError_t launch_skinny(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                         bool *greedy_done) {
+                         bool *greedy_done, bool *draft_done) {
   if constexpr (KC == 128) {
-    if (a.w12_codes) return launch_skinny_as<MT, KC, NS, kLmW12>(a, stream, n_part, greedy_done);
-    if (a.w_blocked) return launch_skinny_as<MT, KC, NS, kLmBlocked>(a, stream, n_part, greedy_done);
+    if (a.w12_codes)
+      return launch_skinny_as<MT, KC, NS, kLmW12>(a, stream, n_part, greedy_done, draft_done);
+    if (a.w_blocked)
+      return launch_skinny_as<MT, KC, NS, kLmBlocked>(a, stream, n_part, greedy_done, draft_done);
   }
-  return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part, greedy_done);
+  return launch_skinny_as<MT, KC, NS, kLmBf16>(a, stream, n_part, greedy_done, draft_done);
 }
 
 // Blocked copy of a bf16 LM head: block (st, s), stored stage-major at index
@@ -1480,15 +1671,16 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
 }
 
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                              bool *zx_done, bool *greedy_done) {
+                              bool *zx_done, bool *greedy_done, bool *draft_done) {
   const int cap = a.rm.B * (a.rm.gamma + 1);
   *zx_done = false;
   if (greedy_done) *greedy_done = false;
+  if (draft_done) *draft_done = false;
   if (a.d % 128 == 0 && cap <= 64) *zx_done = a.zx != nullptr && a.draft_tokens != nullptr;
   if (a.d % 128 == 0) {
-    if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part, greedy_done);
-    if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part, greedy_done);
-    if (cap <= 64) return launch_skinny<4, 128, 2>(a, stream, n_part, greedy_done);
+    if (cap <= 16) return launch_skinny<1, 128, 4>(a, stream, n_part, greedy_done, draft_done);
+    if (cap <= 32) return launch_skinny<2, 128, 3>(a, stream, n_part, greedy_done, draft_done);
+    if (cap <= 64) return launch_skinny<4, 128, 2>(a, stream, n_part, greedy_done, draft_done);
   }
   if (cap <= 16) return launch_stream<1, 64, 256>(a, stream, n_part);
   if (cap <= 32) return launch_stream<2, 64, 128>(a, stream, n_part);
@@ -1535,15 +1727,25 @@ hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_
   return hipGetLastError();
 }
 
+hipError_t launch_merge_decide(const VerifyArgs &a, const DecideArgs &o, int n_part,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(k_merge_decide, dim3(a.rm.B), dim3(kDecideThreads), 0, stream, a, o, n_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_merge(const VerifyArgs &a, int n_part, bool zx_done, hipStream_t stream) {
+  VerifyArgs m = a;
+  if (!zx_done) m.zx = nullptr;
+  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, m, n_part);
+  return hipGetLastError();
+}
+
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
   int n_part = 0;
   bool zx_done = false;
   hipError_t e = launch_contraction(a, stream, &n_part, &zx_done);
   if (e != hipSuccess) return e;
-  VerifyArgs m = a;
-  if (!zx_done) m.zx = nullptr;
-  hipLaunchKernelGGL(k_row_merge, dim3(a.rm.B * (a.rm.gamma + 1)), dim3(256), 0, stream, m, n_part);
-  return hipGetLastError();
+  return launch_row_merge(a, n_part, zx_done, stream);
 }
 
 }  // namespace sdv

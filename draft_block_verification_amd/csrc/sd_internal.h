@@ -33,6 +33,29 @@ struct TilePartial {
 };
 static_assert(sizeof(TilePartial) == 16, "partials are 16 bytes");
 
+// Drafter-row normaliser of one vocabulary chunk (kDraftChunk ids) of one kept draft row.
+struct DraftPart {
+  float m;       // max drafter logit of the chunk (raw, before / T)
+  float pad;
+  double s;      // sum over the chunk of exp((l - m) / T)
+};
+static_assert(sizeof(DraftPart) == 16, "drafter partials are 16 bytes");
+
+// Vocabulary ids per chunk of the rejection kernels (drafter normaliser and draws).
+constexpr int kDraftChunk = 4096;
+
+// What the draw kernels read of request r's decision: the row they sample and its scale
+// constants, written by the decision kernel so the draws need one load before the logits.
+struct DrawRec {
+  int32_t row;     // packed row of the draw (base + a_r), -1 for a request outside the row capacity
+  int32_t acc;     // a_r
+  int32_t qrow;    // drafter row r * gamma + a_r of a residual draw, -1 for the bonus draw from p
+  int32_t pad;
+  float cp, cq;    // T * log-normaliser of that target row and of that drafter row, in fp32
+  int32_t pad2[2];
+};
+static_assert(sizeof(DrawRec) == 32, "draw records are 32 bytes");
+
 // Largest W12 correction-slot count per (64-row, 128-column) region the contraction stages.
 constexpr int kW12MaxCap = 64;
 
@@ -94,6 +117,31 @@ __device__ inline int clamp_len(const int32_t *verify_len, int r, int gamma, WsH
   return L;
 }
 
+// fp64 sum of h[k] * w[k] over eight bf16 pairs (every product is exact in fp64).
+__device__ inline double dot8_f64(const u32x4 &hv, const u32x4 &wv) {
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    part += (double)__uint_as_float(hv[e] << 16) * (double)__uint_as_float(wv[e] << 16);
+    part += (double)__uint_as_float(hv[e] & 0xffff0000u) * (double)__uint_as_float(wv[e] & 0xffff0000u);
+  }
+  return part;
+}
+
+// 2^x by the hardware instruction. It returns no denormals: results below 2^-126 are 0,
+// far below anything the sums and draws resolve (each draw or sum is relative to a row
+// whose weights add up to 1).
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight exp((v - top) / T) = 2^((v - top) * sl), sl = log2(e) / T, of a partial whose
+// maximum is v when a row's partials are merged under the row maximum top. Each partial's
+// own sum is already an fp32 sum of the same hardware exponential, so forming its weight
+// the same way keeps the merged sum at that precision (about 1e-7 relative); the terms
+// are added in fp64.
+__device__ inline double partial_weight(float v, float top, float sl) {
+  return (double)exp2_hw((v - top) * sl);
+}
+
 // Order used for argmax: larger value first, then lower index.
 __device__ inline bool beats(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -133,6 +181,30 @@ struct VerifyArgs {
   int32_t *greedy_accept_len;
   int32_t *greedy_next_token;
   int64_t *greedy_counters;
+  // Rejection verify in one call: the streaming contraction's launch gains workgroups
+  // g_main .. gridDim.x - 1 that write the drafter chunk partials dpart [B][gamma][dchunks]
+  // of every kept draft row (draft_logits bf16 [B][gamma][V]). g_main is the contraction's
+  // own grid, set by its launcher.
+  // qx [B][gamma] receives, with dpart, the drafter logit of each kept row's drafted token.
+  const uint16_t *draft_logits;
+  DraftPart *dpart;
+  float *qx;
+  int dchunks;
+  int g_main;
+};
+
+// Largest gamma whose rows k_merge_decide merges in one workgroup pass (32 row slots).
+constexpr int kDecideMaxGamma = 31;
+
+// Outputs of the rejection decision that k_merge_decide takes after merging the row
+// statistics (with VerifyArgs for the rows and the drafter inputs).
+struct DecideArgs {
+  const float *u_accept;    // [B][gamma]
+  double *lse_q;            // [B][gamma] out: drafter log-normaliser of each kept row
+  DrawRec *rec;             // [B] out: the draw each request takes
+  int32_t *accept_len;      // [B] out
+  int32_t *next_token;      // [B] out (-1 for a request outside the row capacity)
+  int64_t *counters;        // [2] or null
 };
 
 // LM-head formats of the streaming contraction.

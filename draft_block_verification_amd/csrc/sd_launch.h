@@ -22,8 +22,21 @@ hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_
 // a.greedy_accept_len set, *greedy_done (when given) says whether the launch also wrote
 // the greedy statistics and decisions (small streaming grids); otherwise the caller
 // still has to.
+// With a.dpart and a.draft_logits set, a streaming contraction may also write the drafter
+// chunk partials of every kept draft row (workgroups appended to its grid); *draft_done
+// (when given) says whether it did.
 hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_part,
-                              bool *zx_done, bool *greedy_done = nullptr);
+                              bool *zx_done, bool *greedy_done = nullptr,
+                              bool *draft_done = nullptr);
+// Row statistics from the contraction's n_part partial columns (k_row_merge), with the
+// drafted-token logits of a.zx when the contraction formed them (zx_done).
+hipError_t launch_row_merge(const VerifyArgs &a, int n_part, bool zx_done, hipStream_t stream);
+// Rejection verify's row merge and decision (k_merge_decide, gamma <= kDecideMaxGamma):
+// statistics of every verified
+// row, drafter log-normalisers, a_r and the counters, from the contraction's n_part
+// partial columns, the drafter chunk partials and a.zx.
+hipError_t launch_merge_decide(const VerifyArgs &a, const DecideArgs &o, int n_part,
+                               hipStream_t stream);
 
 // Stage-major blocked copy of a bf16 LM head (the layout VerifyArgs::w_blocked reads).
 hipError_t launch_block_lm_head(const uint16_t *W, int V, int d, uint16_t *out,
@@ -45,11 +58,19 @@ hipError_t launch_accept_greedy(const sd_row_stats *stats, const int32_t *draft_
 struct AcceptLayout {
   int chunks;       // vocabulary chunks per row
   size_t lse_q;     // double [B][gamma] drafter log-normalisers (right after the header)
-  size_t acc_a;     // int32 [B] accepted lengths
+  size_t rec;       // DrawRec [B] draw records
+  size_t qx;        // float [B][gamma] drafter logits of the drafted tokens
   size_t dpart;     // drafter chunk partials [B][gamma][chunks]
   size_t csum;      // double [B][chunks][2] draw-weight chunk sums
 };
 size_t accept_workspace_layout(int B, int gamma, int V, AcceptLayout *lay);
+
+// Rejection verify in one call: the contraction (v.logits and v.stats set), the drafter
+// normaliser, k_merge_decide and the draws; v.draft_logits and v.draft_tokens are required.
+hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const float *u_resample,
+                                   int32_t *accept_len, int32_t *next_token, int64_t *counters,
+                                   double *accept_rate, void *accept_workspace,
+                                   hipStream_t stream);
 
 // Rejection acceptance.
 hipError_t launch_accept_rejection(const float *logits, const sd_row_stats *stats,

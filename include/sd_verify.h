@@ -430,6 +430,51 @@ SD_API int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *s
                             int32_t *next_token, int64_t *counters, double *accept_rate,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* LM-head layouts of sd_verify_rejection. */
+enum {
+    SD_LM_HEAD_ROWS = 0,     /* bf16 [V][d]                                              */
+    SD_LM_HEAD_BLOCKED = 1   /* the stage-major blocked copy written by sd_lm_head_block */
+};
+
+/*
+ * Rejection verify of a drafted block in one call (DSpark summary, "Problem definition":
+ * the target checks the block in one pass and rejection sampling keeps the longest
+ * prefix consistent with its distribution; "Architecture": a correction token on the
+ * first rejection, a bonus token when every draft survives): sd_verify_logits at
+ * `temperature` followed by sd_accept_rejection_ex, in fewer launches. The row merge and
+ * the acceptance test run in one kernel; in the streaming regime (d % 128 == 0,
+ * B * (gamma + 1) <= 64) the contraction's launch also normalises the drafter rows when
+ * the GPU has workgroup slots its grid leaves idle.
+ *   hidden, draft_tokens, verify_len, row_offsets, B, gamma, d, V
+ *                as for sd_verify_logits (draft_tokens required)
+ *   lm_head      bf16 [V][d] (lm_head_layout SD_LM_HEAD_ROWS) or its blocked copy
+ *                (SD_LM_HEAD_BLOCKED, streaming regime only, else SD_ESHAPE)
+ *   draft_logits, u_accept, u_resample, temperature (> 0)
+ *                as for sd_accept_rejection
+ *   logits, stats  out, as for sd_verify_logits (both required)
+ *   accept_len, next_token, counters, accept_rate (NULL: not computed)
+ *                out, as for sd_accept_rejection_ex
+ *   verify_workspace  sd_verify_workspace_bytes(B, gamma, d, V) bytes
+ *   accept_workspace  sd_accept_workspace_bytes(B, gamma, V) bytes
+ * The logits, argmax, top-1/top-2, drafted-token logits, accepted lengths, tokens,
+ * counters and flags are those of the two separate calls; the per-row log-normalisers
+ * (stats lse and the drafter's) are summed in another order and agree with them to
+ * fp64 rounding.
+ * Errors: those of sd_verify_logits and sd_accept_rejection_ex; SD_EINVAL for an unknown
+ * lm_head_layout.
+ */
+SD_API int32_t sd_verify_rejection(const uint16_t *hidden, const uint16_t *lm_head,
+                                   int32_t lm_head_layout, const uint16_t *draft_logits,
+                                   const int32_t *draft_tokens, const int32_t *verify_len,
+                                   const int32_t *row_offsets, const float *u_accept,
+                                   const float *u_resample, int32_t B, int32_t gamma, int32_t d,
+                                   int32_t V, float temperature, float *logits,
+                                   sd_row_stats *stats, int32_t *accept_len,
+                                   int32_t *next_token, int64_t *counters, double *accept_rate,
+                                   void *verify_workspace, size_t verify_workspace_bytes,
+                                   void *accept_workspace, size_t accept_workspace_bytes,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

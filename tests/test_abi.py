@@ -193,3 +193,35 @@ def test_verify_greedy_noalloc_host_validation():
     assert sd.verify_workspace_bytes(32, 16, 4096, 151936) > sd.NOALLOC_SCRATCH_BYTES
     assert _noalloc(B=32, g=16, d=4096, V=151936) == 6
     assert sd.verify_workspace_bytes(1, 9, 2048, 32768) <= sd.NOALLOC_SCRATCH_BYTES
+
+
+def _verify_rejection(**kw):
+    a = dict(hidden=FAKE, lm_head=FAKE, layout=0, dlog=FAKE, draft=FAKE, vlen=None, offs=None,
+             ua=FAKE, ur=FAKE, B=1, g=4, d=256, V=1024, T=1.0, logits=FAKE, stats=FAKE,
+             acc=FAKE, nxt=FAKE, cnt=None, rate=None, wsv=FAKE, wsv_bytes=1 << 30, wsa=FAKE,
+             wsa_bytes=1 << 30, stream=None)
+    a.update(kw)
+    i32 = ctypes.c_int32
+    return lib.sd_verify_rejection(
+        a["hidden"], a["lm_head"], i32(a["layout"]), a["dlog"], a["draft"], a["vlen"],
+        a["offs"], a["ua"], a["ur"], i32(a["B"]), i32(a["g"]), i32(a["d"]), i32(a["V"]),
+        ctypes.c_float(a["T"]), a["logits"], a["stats"], a["acc"], a["nxt"], a["cnt"],
+        a["rate"], a["wsv"], ctypes.c_size_t(a["wsv_bytes"]), a["wsa"],
+        ctypes.c_size_t(a["wsa_bytes"]), a["stream"])
+
+
+def test_verify_rejection_host_validation():
+    assert _verify_rejection(layout=2) == 1            # unknown LM-head layout
+    assert _verify_rejection(logits=None) == 1         # the draws need the logits
+    assert _verify_rejection(dlog=None) == 1
+    assert _verify_rejection(ur=None) == 1
+    assert _verify_rejection(T=0.0) == 1               # greedy has its own call
+    assert _verify_rejection(vlen=FAKE) == 1           # lengths without offsets
+    assert _verify_rejection(g=65) == 2
+    assert _verify_rejection(layout=1, d=200) == 2     # blocked copy: d % 128 == 0 only
+    assert _verify_rejection(layout=1, B=16) == 2      # blocked copy: streaming regime only
+    assert _verify_rejection(dlog=MISALIGNED) == 3
+    assert _verify_rejection(rate=ctypes.c_void_p(0x10004)) == 3
+    assert _verify_rejection(wsv_bytes=100) == 4
+    assert _verify_rejection(wsa=None) == 4
+    assert _verify_rejection(wsa_bytes=100) == 4

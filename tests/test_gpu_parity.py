@@ -238,6 +238,71 @@ def test_fused_greedy_matches_separate_calls(case):
             assert torch.equal(a, b)
 
 
+REJ_FUSED = [
+    # Streaming contraction with idle workgroup slots (the drafter rows are normalised in
+    # its launch), without them (65536 ids: 1024 slabs, the grid fills every slot, so a
+    # separate drafter launch runs), the register-staged streaming kernel (d % 128 != 0:
+    # the drafted-token logits come from the drafter launch too), the tiled kernel,
+    # gamma = 64 (three passes of row slots), many small requests, and the blocked head.
+    ("rej-skinny-appended", dict(B=1, gamma=16, d=512, V=20000, truncate=False)),
+    ("rej-skinny-full-grid", dict(B=1, gamma=9, d=256, V=65536, truncate=False)),
+    ("rej-stream-d200", dict(B=2, gamma=12, d=200, V=5001, truncate=True)),
+    ("rej-tiled", dict(B=20, gamma=16, d=256, V=7000, truncate=True)),
+    ("rej-gamma64", dict(B=2, gamma=64, d=64, V=4099, truncate=False)),
+    ("rej-many", dict(B=300, gamma=3, d=64, V=129, truncate=True)),
+    ("rej-blocked", dict(B=3, gamma=16, d=256, V=9000, truncate=True, blocked=True)),
+]
+
+
+@pytest.mark.parametrize("case", REJ_FUSED, ids=lambda c: c[0])
+def test_fused_rejection_matches_separate_calls(case):
+    """sd_verify_rejection against sd_verify_logits + sd_accept_rejection_ex: logits,
+    argmax, top-1/top-2, drafted-token logits, accepted lengths, tokens, counters,
+    acceptance rates and flags equal; the log-normalisers (summed in another order) to
+    fp64 rounding."""
+    name, over = case
+    over = dict(over)
+    blocked = over.pop("blocked", False)
+    w = workload("ragged-b32", T=0.9, geo_p=(0.2,), name=name, **over)
+    W = make_weights(w)
+    W_dev = bf16_dev(W)
+    if blocked:
+        W_dev = sd.BlockedWeights(W_dev)
+    for step in range(2):
+        say(name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={step}")
+        ds = upload_step(make_step(w, W, step))
+        outs = []
+        for fused in (True, False):
+            vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold,
+                                fused=fused, accept_rate=True)
+            vr.counters.zero_()
+            vr.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf, ds.draft_logits, ds.u_accept,
+                   ds.u_resample)
+            torch.cuda.synchronize()
+            M = int(vr.row_offsets[-1].item()) if w.truncate else w.B * (w.gamma + 1)
+            st = sd.stats_to_numpy(vr.stats)[:M]
+            lse_q = (vr.ws_accept[256:256 + 8 * w.B * w.gamma].cpu().numpy().view(np.float64)
+                     .reshape(w.B, w.gamma))
+            outs.append(dict(st=st, logits=vr.logits[:M].clone(), acc=vr.accept_len.clone(),
+                             nxt=vr.next_token.clone(), cnt=vr.counters.clone(),
+                             rate=vr.accept_rate.clone(), lse_q=lse_q,
+                             vlen=None if vr.verify_len is None else vr.verify_len.clone(),
+                             flags=sd.device_flags(vr.ws_verify) | sd.device_flags(vr.ws_accept)))
+        f, s = outs
+        assert f["flags"] == 0 and s["flags"] == 0
+        assert torch.equal(f["logits"], s["logits"])
+        for k in ("argmax", "top1", "top2", "pos", "z_draft"):
+            assert np.array_equal(f["st"][k], s["st"][k]), k
+        assert np.allclose(f["st"]["lse"], s["st"]["lse"], rtol=1e-13, atol=1e-13)
+        L = (f["vlen"].cpu().numpy() if f["vlen"] is not None
+             else np.full(w.B, w.gamma))
+        kept = np.arange(w.gamma)[None, :] < L[:, None]
+        assert np.allclose(f["lse_q"][kept], s["lse_q"][kept], rtol=1e-13, atol=1e-13)
+        for k in ("acc", "nxt", "cnt"):
+            assert torch.equal(f[k], s[k]), k
+        assert torch.allclose(f["rate"], s["rate"], rtol=0, atol=1e-12)
+
+
 def test_rejection_lossless_on_gpu():
     """Bigram target and drafter over V = 8: emitted first tokens follow the target."""
     from scipy import special, stats as sstats
