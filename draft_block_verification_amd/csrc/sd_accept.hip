@@ -475,18 +475,21 @@ __global__ __launch_bounds__(256) void k_draw_partial(RejArgs a, int rows) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
-  __shared__ double s_d[8];
-  __shared__ int s_i[12];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (a.rate) rate_finalize(a, r);
-  DrawRow d;
-  int arow, acc;
-  if (!draw_row(a, r, &d, &arow, &acc)) return;
-  const int gamma = a.rm.gamma;
-  const double *cs = a.csum + (size_t)r * a.C * 2;
-  // Chunk sums in chunk order: thread t owns chunks t*K .. t*K + K - 1 (K = ceil(C/256)),
-  // an inclusive block scan gives every chunk's running sum.
+// Where request r's draw lands among its chunks, from the chunk sums cs [C][2] (residual
+// or bonus weight, p weight) in chunk order: thread t owns chunks t*K .. t*K + K - 1
+// (K = ceil(C/256)) and an inclusive block scan gives every chunk's running sum. The
+// hit is the first chunk whose running sum passes u * S, else (rounding) the last chunk
+// with positive weight (last_pos), or -1 when no id has weight; col says whether the
+// residual had no mass and p is drawn instead; carry is the running sum before the hit.
+// Every thread of the workgroup calls it.
+struct DrawLoc {
+  int hit, last_pos, col;
+  double carry, thresh;
+};
+
+__device__ DrawLoc draw_locate(const RejArgs &a, int r, int acc, bool has_q, const double *cs,
+                               double *s_d, int *s_i) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int use_p = 0;
   double S = 0.0, excl = 0.0, own = 0.0;
   const int K = (a.C + 255) / 256, c0 = tid * K;
@@ -507,14 +510,12 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
     excl = before + (incl - own);
     S = ((s_d[0] + s_d[1]) + s_d[2]) + s_d[3];
     __syncthreads();
-    if (S != 0.0 || !d.q || pass == 1) break;
+    if (S != 0.0 || !has_q || pass == 1) break;
     // No residual mass (p == q at this row): draw from p instead.
     if (tid == 0) raise_flag(a.ws, SD_FLAG_NO_RESIDUAL);
     use_p = 1;
   }
-  const double thresh = (double)a.u_resample[(size_t)r * (gamma + 1) + acc] * S;
-  // First chunk whose running sum passes thresh; else (rounding) the last chunk with
-  // positive weight.
+  const double thresh = (double)a.u_resample[(size_t)r * (a.rm.gamma + 1) + acc] * S;
   int first = 0x7fffffff, lastc = -1;
   if (S > 0.0) {
     double run = excl;
@@ -549,18 +550,19 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
     }
   }
   __syncthreads();
-  const int hit = s_i[0], last_pos = s_i[1], col = s_i[2];
-  if (hit < 0) {                      // no weight at all: fall back to the target argmax
-    if (tid == 0) a.next_token[r] = a.stats[arow].argmax;
-    return;
-  }
-  if (col == 1) d.q = nullptr;
-  const double carry = s_d[0];
-  // Scan the crossing chunk: kPer consecutive ids per thread, exclusive scan of the
-  // per-thread sums, then the crossing thread walks its ids.
-  const int v0 = hit * kChunk + tid * kPer;
-  float w[kPer];
-  double mine = 0.0;
+  DrawLoc loc;
+  loc.hit = s_i[0];
+  loc.last_pos = s_i[1];
+  loc.col = s_i[2];
+  loc.carry = s_d[0];
+  loc.thresh = thresh;
+  __syncthreads();   // s_d and s_i are reused by the caller
+  return loc;
+}
+
+// Weights of the kPer consecutive ids v0 .. v0 + kPer - 1 of a draw row (0 past V).
+__device__ inline void draw_thread_weights(const RejArgs &a, const DrawRow &d, int v0,
+                                           float (&w)[kPer]) {
   if ((a.V & 7) == 0 && v0 + kPer <= a.V) {
 #pragma unroll
     for (int h = 0; h < kPer / 4; ++h) {
@@ -587,6 +589,36 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
       w[e] = x;
     }
   }
+}
+
+// Residual weights max(0, p - q) of the same ids from their p weights wp (the arithmetic
+// of draw_thread_weights, so the values are the same bits).
+__device__ inline void draw_thread_residual(const RejArgs &a, const DrawRow &d, int v0,
+                                            const float (&wp)[kPer], float (&wr)[kPer]) {
+  if ((a.V & 7) == 0 && v0 + kPer <= a.V) {
+#pragma unroll
+    for (int h = 0; h < kPer / 8; ++h) {
+      const u32x4 qv = *reinterpret_cast<const u32x4 *>(d.q + v0 + 8 * h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ql = __uint_as_float((i & 1) ? (qv[i >> 1] & 0xffff0000u) : (qv[i >> 1] << 16));
+        wr[8 * h + i] = fmaxf(wp[8 * h + i] - prob_of(ql, d.qs), 0.f);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      wr[e] = v0 + e < a.V ? fmaxf(wp[e] - prob_of(bf16_to_f32(d.q[v0 + e]), d.qs), 0.f) : 0.f;
+  }
+}
+
+// The token inside the hit chunk: thread t holds the weights w of ids v0 = hit * kChunk +
+// t * kPer ..; an exclusive scan of the per-thread sums after loc.carry, then the thread
+// whose ids cross loc.thresh walks them (the last positive id when rounding leaves none).
+__device__ void draw_in_chunk(const RejArgs &a, int r, const float (&w)[kPer], int v0,
+                              const DrawLoc &loc, double *s_d, int *s_i) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double mine = 0.0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) mine += (double)w[e];
   double incl = mine;
@@ -599,15 +631,15 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   __syncthreads();
   double before = 0.0;
   for (int q = 0; q < wave; ++q) before += s_d[2 + q];
-  const double base = carry + (before + (incl - mine));
+  const double base = loc.carry + (before + (incl - mine));
   int cross = 0x7fffffff, lastp = -1;
   for (int e = kPer - 1; e >= 0; --e)
     if (w[e] > 0.f) { lastp = v0 + e; break; }
-  if (!last_pos && base + mine > thresh) {
+  if (!loc.last_pos && base + mine > loc.thresh) {
     double run = 0.0;
     for (int e = 0; e < kPer; ++e) {
       run += (double)w[e];
-      if (base + run > thresh) { cross = v0 + e; break; }
+      if (base + run > loc.thresh) { cross = v0 + e; break; }
     }
     if (cross == 0x7fffffff && lastp >= 0) cross = lastp;
   }
@@ -621,8 +653,109 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   if (tid == 0) {
     int c = s_i[4], l = s_i[8];
     for (int q = 1; q < 4; ++q) { c = min(c, s_i[4 + q]); l = max(l, s_i[8 + q]); }
-    a.next_token[r] = (!last_pos && c != 0x7fffffff) ? c : l;
+    a.next_token[r] = (!loc.last_pos && c != 0x7fffffff) ? c : l;
   }
+}
+
+__global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
+  __shared__ double s_d[8];
+  __shared__ int s_i[12];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (a.rate) rate_finalize(a, r);
+  DrawRow d;
+  int arow, acc;
+  if (!draw_row(a, r, &d, &arow, &acc)) return;
+  const DrawLoc loc = draw_locate(a, r, acc, d.q != nullptr, a.csum + (size_t)r * a.C * 2, s_d, s_i);
+  if (loc.hit < 0) {                  // no weight at all: fall back to the target argmax
+    if (tid == 0) a.next_token[r] = a.stats[arow].argmax;
+    return;
+  }
+  if (loc.col == 1) d.q = nullptr;
+  const int v0 = loc.hit * kChunk + tid * kPer;
+  float w[kPer];
+  draw_thread_weights(a, d, v0, w);
+  draw_in_chunk(a, r, w, v0, loc, s_d, s_i);
+}
+
+// The draw in one launch, for grids whose workgroups all run at once (B * C <= kDrawOnePassMax):
+// workgroup (c, r) forms the weights of its chunk's ids (kPer consecutive ids per thread)
+// for both the residual (or bonus) column and p, sums them, and publishes the two sums
+// with device-scope atomic stores into slots the decision kernel set to kUnpublished.
+// Each workgroup then waits for all C sums of its request, locates the draw exactly as
+// k_draw_finalize does, and the workgroup holding the hit chunk finishes the draw from
+// the weights still in its registers. The wait is bounded: a workgroup that has polled a
+// slot kDrawSpinLimit times raises SD_FLAG_DRAW_WAIT and writes -1, and the request's
+// token is then not valid.
+constexpr int kDrawOnePassMax = 256;
+constexpr int kDrawSpinLimit = 1 << 20;
+__device__ inline unsigned long long published_bits(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  return b == kUnpublished ? 0x7ff8000000000000ull : b;   // never the empty-slot pattern
+}
+
+__global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a) {
+  __shared__ double s_d[8];
+  __shared__ int s_i[12];
+  __shared__ double s_cs[2 * kDrawOnePassMax];
+  __shared__ int s_late;
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  DrawRow d;
+  int arow, acc;
+  if (!draw_row(a, r, &d, &arow, &acc)) return;
+  const int v0 = c * kChunk + tid * kPer;
+  float wp[kPer], wr[kPer];
+  {
+    DrawRow dp = d;
+    dp.q = nullptr;
+    draw_thread_weights(a, dp, v0, wp);
+  }
+  if (d.q) {
+    draw_thread_residual(a, d, v0, wp, wr);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) wr[e] = wp[e];
+  }
+  double sr = 0.0, sp = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) { sr += (double)wr[e]; sp += (double)wp[e]; }
+  sr = block_sum_d(sr, s_d);
+  sp = block_sum_d(sp, s_d);
+  unsigned long long *pub = reinterpret_cast<unsigned long long *>(a.csum) + (size_t)r * a.C * 2;
+  if (tid == 0) {
+    __hip_atomic_store(pub + 2 * c, published_bits(sr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(pub + 2 * c + 1, published_bits(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_late = 0;
+  }
+  __syncthreads();
+  for (int k = tid; k < 2 * a.C; k += 256) {
+    unsigned long long v = kUnpublished;
+    for (int it = 0; it < kDrawSpinLimit; ++it) {
+      v = __hip_atomic_load(pub + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v != kUnpublished) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (v == kUnpublished) s_late = 1;
+    s_cs[k] = __longlong_as_double((long long)v);
+  }
+  __syncthreads();
+  if (s_late) {
+    if (tid == 0) {
+      raise_flag(a.ws, SD_FLAG_DRAW_WAIT);
+      a.next_token[r] = -1;
+    }
+    return;
+  }
+  const DrawLoc loc = draw_locate(a, r, acc, d.q != nullptr, s_cs, s_d, s_i);
+  if (loc.hit < 0) {
+    if (c == 0 && tid == 0) a.next_token[r] = a.stats[arow].argmax;
+    return;
+  }
+  if (loc.hit != c) return;
+  if (loc.col == 1) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) wr[e] = wp[e];
+  }
+  draw_in_chunk(a, r, wr, v0, loc, s_d, s_i);
 }
 
 // Second grid dimension for a row range (the hardware bounds it at 65535).
@@ -773,14 +906,23 @@ hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const fl
     }
     if ((e = launch_draft_partial(a, stream)) != hipSuccess) return e;
   }
+  // The draw in one launch when all of its workgroups fit on the chip at once and no
+  // acceptance rates ride along.
+  const bool onepass_draw =
+      one_pass && !accept_rate && (long long)v.rm.B * a.C <= kDrawOnePassMax;
   if (one_pass) {
-    DecideArgs o{u_accept, a.lse_q, a.rec, accept_len, next_token, counters};
+    DecideArgs o{u_accept, a.lse_q, a.rec, accept_len, next_token, counters,
+                 onepass_draw ? reinterpret_cast<unsigned long long *>(a.csum) : nullptr, a.C};
     e = launch_merge_decide(v, o, n_part, stream);
   } else {
     hipLaunchKernelGGL(k_accept_decide, dim3(v.rm.B), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
+  if (onepass_draw) {
+    hipLaunchKernelGGL(k_draw_onepass, dim3(a.C, v.rm.B), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   return launch_draws(a, stream);
 }
 

@@ -1396,6 +1396,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_merge_decide(VerifyArgs a, D
   const int xl = a.draft_tokens[rj];
   const float u = o.u_accept[rj];
   const float lx = a.qx[rj];   // drafter logit of the token, left by the drafter normaliser
+  if (o.pub)
+    for (int k = tid; k < 2 * o.pub_chunks; k += kDecideThreads)
+      o.pub[(size_t)r * 2 * o.pub_chunks + k] = kUnpublished;
   DraftPart dq[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) dq[i] = a.dpart[rj * C + min(sub + kDecideLanes * i, C - 1)];

@@ -56,6 +56,9 @@ struct DrawRec {
 };
 static_assert(sizeof(DrawRec) == 32, "draw records are 32 bytes");
 
+// Bit pattern of a chunk-sum slot that the one-launch draw has not yet published.
+constexpr unsigned long long kUnpublished = ~0ull;
+
 // Largest W12 correction-slot count per (64-row, 128-column) region the contraction stages.
 constexpr int kW12MaxCap = 64;
 
@@ -205,6 +208,10 @@ struct DecideArgs {
   int32_t *accept_len;      // [B] out
   int32_t *next_token;      // [B] out (-1 for a request outside the row capacity)
   int64_t *counters;        // [2] or null
+  // Chunk-sum slots [B][chunks][2] of the one-launch draw that follows, set here to
+  // kUnpublished; null when the draw runs in two launches.
+  unsigned long long *pub;
+  int pub_chunks;
 };
 
 // LM-head formats of the streaming contraction.

@@ -77,7 +77,10 @@ enum {
 enum {
     SD_FLAG_VERIFY_LEN = 1,   /* a verify_len entry was outside [0, gamma] and was clamped */
     SD_FLAG_ROW_OFFSETS = 2,  /* row_offsets disagreed with verify_len or overflowed the row capacity */
-    SD_FLAG_NO_RESIDUAL = 4   /* a residual max(0, p - q) had no positive mass; drew from p instead */
+    SD_FLAG_NO_RESIDUAL = 4,  /* a residual max(0, p - q) had no positive mass; drew from p instead */
+    SD_FLAG_DRAW_WAIT = 8     /* sd_verify_rejection's one-launch draw waited too long for its
+                                 other workgroups (they could not all run at once); the
+                                 tokens of that call are not valid */
 };
 
 /* Per verified row statistics (32 bytes, 8-byte aligned). */

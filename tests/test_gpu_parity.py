@@ -272,9 +272,11 @@ def test_fused_rejection_matches_separate_calls(case):
         say(name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={step}")
         ds = upload_step(make_step(w, W, step))
         outs = []
-        for fused in (True, False):
+        # The fused call without rates (small grids draw in one launch), with rates (two
+        # draw launches), then the separate calls with rates.
+        for fused, rate in ((True, False), (True, True), (False, True)):
             vr = sd.VerifyRound(w.B, w.gamma, w.d, w.V, w.T, w.truncate, w.threshold,
-                                fused=fused, accept_rate=True)
+                                fused=fused, accept_rate=rate)
             vr.counters.zero_()
             vr.run(ds.hidden, W_dev, ds.draft_tokens, ds.conf, ds.draft_logits, ds.u_accept,
                    ds.u_resample)
@@ -285,22 +287,24 @@ def test_fused_rejection_matches_separate_calls(case):
                      .reshape(w.B, w.gamma))
             outs.append(dict(st=st, logits=vr.logits[:M].clone(), acc=vr.accept_len.clone(),
                              nxt=vr.next_token.clone(), cnt=vr.counters.clone(),
-                             rate=vr.accept_rate.clone(), lse_q=lse_q,
+                             rate=None if vr.accept_rate is None else vr.accept_rate.clone(),
+                             lse_q=lse_q,
                              vlen=None if vr.verify_len is None else vr.verify_len.clone(),
                              flags=sd.device_flags(vr.ws_verify) | sd.device_flags(vr.ws_accept)))
-        f, s = outs
-        assert f["flags"] == 0 and s["flags"] == 0
-        assert torch.equal(f["logits"], s["logits"])
-        for k in ("argmax", "top1", "top2", "pos", "z_draft"):
-            assert np.array_equal(f["st"][k], s["st"][k]), k
-        assert np.allclose(f["st"]["lse"], s["st"]["lse"], rtol=1e-13, atol=1e-13)
-        L = (f["vlen"].cpu().numpy() if f["vlen"] is not None
-             else np.full(w.B, w.gamma))
-        kept = np.arange(w.gamma)[None, :] < L[:, None]
-        assert np.allclose(f["lse_q"][kept], s["lse_q"][kept], rtol=1e-13, atol=1e-13)
-        for k in ("acc", "nxt", "cnt"):
-            assert torch.equal(f[k], s[k]), k
-        assert torch.allclose(f["rate"], s["rate"], rtol=0, atol=1e-12)
+        s = outs[2]
+        for f in outs[:2]:
+            assert f["flags"] == 0 and s["flags"] == 0
+            assert torch.equal(f["logits"], s["logits"])
+            for k in ("argmax", "top1", "top2", "pos", "z_draft"):
+                assert np.array_equal(f["st"][k], s["st"][k]), k
+            assert np.allclose(f["st"]["lse"], s["st"]["lse"], rtol=1e-13, atol=1e-13)
+            L = (f["vlen"].cpu().numpy() if f["vlen"] is not None
+                 else np.full(w.B, w.gamma))
+            kept = np.arange(w.gamma)[None, :] < L[:, None]
+            assert np.allclose(f["lse_q"][kept], s["lse_q"][kept], rtol=1e-13, atol=1e-13)
+            for k in ("acc", "nxt", "cnt"):
+                assert torch.equal(f[k], s[k]), k
+        assert torch.allclose(outs[1]["rate"], s["rate"], rtol=0, atol=1e-12)
 
 
 def test_rejection_lossless_on_gpu():
