@@ -231,9 +231,9 @@ __global__ __launch_bounds__(256) void k_gemm_stream(VerifyArgs a) {
     for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4 *>(S + buf * STAGE + l_off[i]) = R[i];
   };
 
-  f32x4 acc[MT];
+  f32x4 acc[MT], cacc[MT];                   // cacc: W12 corrected weights' products
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MT; ++i) acc[i] = cacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int br = 16 * wn + (lane & 15);
   RowAcc run = row_acc_init();                  // running stats of row tid / (256 / CR)
 
@@ -620,9 +620,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
                                        (LDSP void *)(dst + HOFF + (wave + 4 * j) * 1024), 16, 0, 0);
   };
 
-  f32x4 acc[MT];
+  f32x4 acc[MT], cacc[MT];                   // cacc: W12 corrected weights' products
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MT; ++i) acc[i] = cacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   RowAcc run[MT];                            // running statistics of row 16 i + fr
 #pragma unroll
   for (int i = 0; i < MT; ++i) run[i] = row_acc_init();
@@ -646,35 +646,15 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     const LDSP uint16_t *Hb = Sb + HOFF / 2;                     // hidden rows
     const LDSP uint32_t *Wq = (const LDSP uint32_t *)Sb;          // W12 groups
     const LDSP uint32_t *Cb = (const LDSP uint32_t *)(Sb + WBYTES / 2);   // correction slots
-    // W12 correction slots of this stage: lane l holds slot l; one ballot per k-step
-    // picks the slots in this wave's rows whose column falls in that k-step.
-    uint32_t cent = 0u;
-    unsigned long long cmask[KC / 32] = {};
-    if (W12) {
-      cent = lane < cap ? Cb[lane] : 0u;
-      const bool mine = cent != 0u && (int)((cent >> 11) & 3u) == wave;   // row_local / 16
-#pragma unroll
-      for (int s = 0; s < KC / 32; ++s) cmask[s] = __ballot(mine && (int)((cent >> 5) & 3u) == s);
-    }
+    // W12 correction slots of this stage: lane l holds slot l.
+    const uint32_t cent = W12 && lane < cap ? Cb[lane] : 0u;
 #pragma unroll
     for (int s = 0; s < KC / 32; ++s) {
       const int c = 4 * s + fc;
       bf16x8 b;
       if (W12) {
         const int o = (br * KC * 3 / 2 + 12 * (c ^ (4 * w12_block_swz(br)))) / 4;
-        u32x4 w = w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1);
-        // A corrected weight is coded as a signed zero; the lane holding its row and
-        // 8-column chunk puts the exact bits in its place before the MFMA.
-        for (unsigned long long mm = cmask[s]; mm; mm &= mm - 1) {
-          const uint32_t ent = (uint32_t)__builtin_amdgcn_readlane((int)cent, __ffsll((long long)mm) - 1);
-          if ((int)((ent >> 7) & 15u) == fr && (int)((ent >> 3) & 15u) == c) {
-            const uint32_t q = (ent >> 1) & 3u, sh = (ent & 1u) * 16u;
-            const uint32_t keep = ~(0xFFFFu << sh), put = (ent >> 16) << sh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)i == q ? ((w[i] & keep) | put) : w[i];
-          }
-        }
-        b = __builtin_bit_cast(bf16x8, w);
+        b = __builtin_bit_cast(bf16x8, w12_decode8(Wq[o], Wq[o + 1], Wq[o + 2], a.w12_lut0, a.w12_lut1));
       } else {
         b = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Sb + br * KC + 8 * (c ^ (br & 15))));
       }
@@ -683,6 +663,27 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         const int hr = 16 * i + fr;
         const bf16x8 av = __builtin_bit_cast(bf16x8, *(const LDSP u32x4 *)(Hb + hr * KC + 8 * (c ^ (hr & 15))));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, av, acc[i], 0, 0, 0);
+      }
+    }
+    if (W12) {
+      // A corrected weight is coded as a signed zero, so the MFMAs left out its products;
+      // they go into separate accumulators after the stage's MFMAs are issued, off the
+      // MFMA operands' path. Each of this wave's slots (row_local / 16 == wave) adds
+      // h[m][k] * w to z[m][v] in the lanes holding vocabulary row v, one hidden row each.
+      for (unsigned long long mm = __ballot(cent != 0u && (int)((cent >> 11) & 3u) == wave); mm;
+           mm &= mm - 1) {
+        const uint32_t ent = (uint32_t)__builtin_amdgcn_readlane((int)cent, __ffsll((long long)mm) - 1);
+        const int kl = ent & 127u, q = ent >> 7 & 3u;
+        if ((int)((ent >> 9) & 3u) == fc) {
+          const float w = __uint_as_float(ent & 0xffff0000u);
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int hr = 16 * i + fr;
+            const float h = bf16_to_f32(Hb[hr * KC + 8 * ((kl >> 3) ^ (hr & 15)) + (kl & 7)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cacc[i][e] += e == q ? h * w : 0.f;
+          }
+        }
       }
     }
     if (t % nst == 0) {
@@ -723,6 +724,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
       // holds row 16 i + fr at the four consecutive vocabulary ids vb .. vb + 3; reduce
       // in registers, then over the four lanes that share fr.
       const int vb = (g + (t / nst) * G) * BN + 16 * wave + 4 * fc;
+      if (W12) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          acc[i] += cacc[i];
+          cacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int m = 16 * i + fr;
