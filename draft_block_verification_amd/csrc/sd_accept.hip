@@ -677,7 +677,8 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
   draw_in_chunk(a, r, w, v0, loc, s_d, s_i);
 }
 
-// The draw in one launch, for grids whose workgroups all run at once (B * C <= kDrawOnePassMax):
+// The draw in one launch, for grids whose workgroups the chip holds all at once (C <=
+// kDrawOnePassMaxChunks and B * C no more than the resident workgroups):
 // workgroup (c, r) forms the weights of its chunk's ids (kPer consecutive ids per thread)
 // for both the residual (or bonus) column and p, sums them, and publishes the two sums
 // with device-scope atomic stores into slots the decision kernel set to kUnpublished.
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
 // the weights still in its registers. The wait is bounded: a workgroup that has polled a
 // slot kDrawSpinLimit times raises SD_FLAG_DRAW_WAIT and writes -1, and the request's
 // token is then not valid.
-constexpr int kDrawOnePassMax = 256;
+constexpr int kDrawOnePassMaxChunks = 256;
 constexpr int kDrawSpinLimit = 1 << 20;
 __device__ inline unsigned long long published_bits(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
@@ -696,7 +697,7 @@ __device__ inline unsigned long long published_bits(double v) {
 __global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a) {
   __shared__ double s_d[8];
   __shared__ int s_i[12];
-  __shared__ double s_cs[2 * kDrawOnePassMax];
+  __shared__ double s_cs[2 * kDrawOnePassMaxChunks];
   __shared__ int s_late;
   const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   DrawRow d;
@@ -906,10 +907,12 @@ hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const fl
     }
     if ((e = launch_draft_partial(a, stream)) != hipSuccess) return e;
   }
-  // The draw in one launch when all of its workgroups fit on the chip at once and no
-  // acceptance rates ride along.
+  // The draw in one launch when the chip holds all of its workgroups at once (each then
+  // runs to its wait, so the wait ends even beside other work) and no acceptance rates
+  // ride along.
   const bool onepass_draw =
-      one_pass && !accept_rate && (long long)v.rm.B * a.C <= kDrawOnePassMax;
+      one_pass && !accept_rate && a.C <= kDrawOnePassMaxChunks &&
+      (long long)v.rm.B * a.C <= resident_workgroups(reinterpret_cast<const void *>(&k_draw_onepass));
   if (one_pass) {
     DecideArgs o{u_accept, a.lse_q, a.rec, accept_len, next_token, counters,
                  onepass_draw ? reinterpret_cast<unsigned long long *>(a.csum) : nullptr, a.C};

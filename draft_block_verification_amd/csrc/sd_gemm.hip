@@ -1759,4 +1759,6 @@ hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
   return launch_row_merge(a, n_part, zx_done, stream);
 }
 
+int resident_workgroups(const void *fn) { return resident_blocks(fn); }
+
 }  // namespace sdv

@@ -38,6 +38,9 @@ hipError_t launch_row_merge(const VerifyArgs &a, int n_part, bool zx_done, hipSt
 hipError_t launch_merge_decide(const VerifyArgs &a, const DecideArgs &o, int n_part,
                                hipStream_t stream);
 
+// Workgroups of 256 threads of kernel fn that the current device holds at once.
+int resident_workgroups(const void *fn);
+
 // Stage-major blocked copy of a bf16 LM head (the layout VerifyArgs::w_blocked reads).
 hipError_t launch_block_lm_head(const uint16_t *W, int V, int d, uint16_t *out,
                                 hipStream_t stream);
