@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--preheat-seconds", type=float, default=1.0,
+                    help="before the first timed region, run untimed steps for this long, so "
+                         "that the timed steps see the clocks the GPU sustains under this load "
+                         "(0 = none)")
     ap.add_argument("--workload", default="concurrency-b128",
                     help="tiny-greedy, greedy-block9, rejection-b1, ragged-b32 or "
                          "concurrency-b128 (default)")
@@ -215,8 +219,22 @@ def main():
         sd.sd_verify_contraction(st["hidden"], W_dev[i % n_copies], vr.verify_len,
                                  vr.row_offsets, w.T, vr.logits, vr.ws_verify)
 
+    preheated = [args.preheat_seconds <= 0]
+
     def timed(fn, n, warm):
-        """Run fn(i) for n steps after `warm` untimed ones; returns milliseconds."""
+        """Run fn(i) for n steps after `warm` untimed ones; returns milliseconds. Before the
+        first timed region, untimed steps run for --preheat-seconds (the clocks ramp over
+        the first tens of milliseconds of sustained load)."""
+        if not preheated[0]:
+            t_end = time.time() + args.preheat_seconds
+            i = 0
+            while time.time() < t_end:
+                with torch.cuda.stream(stream):
+                    for _ in range(8):
+                        fn(i)
+                        i += 1
+                torch.cuda.synchronize()
+            preheated[0] = True
         with torch.cuda.stream(stream):
             for i in range(warm):
                 fn(i)
@@ -364,6 +382,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": Wu,
+        "preheat_s": args.preheat_seconds,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
