@@ -90,6 +90,13 @@ SHAPES = [
     ("tiled-rows-255", 15, 16, 128, 3000, 1.0, False),
     ("tiled-rows-513", 27, 18, 64, 2000, 0.0, False),
     ("tiled-rows-775", 25, 30, 64, 1500, 0.9, False),
+    # More partial columns per row (547 vocabulary tiles of 128) than the rejection
+    # decision holds in registers (512): its second loop over the partials.
+    ("tiled-d96-547-tiles-rej", 5, 16, 96, 70000, 1.0, True),
+    # Vocabularies of 256 and 269 chunks of 4096: the largest one-launch draw, and the
+    # first one that falls back to two launches.
+    ("vocab-256-chunks-rej", 1, 2, 8, 1048000, 1.0, False),
+    ("vocab-269-chunks-rej", 1, 2, 8, 1100000, 0.8, False),
 ]
 
 
