@@ -78,7 +78,7 @@ ROW_STATS_DTYPE = np.dtype([("argmax", "<i4"), ("top1", "<f4"), ("top2", "<f4"),
                             ("lse", "<f8"), ("z_draft", "<f8")])
 assert ROW_STATS_DTYPE.itemsize == 32
 
-FLAG_VERIFY_LEN, FLAG_ROW_OFFSETS, FLAG_NO_RESIDUAL, FLAG_DRAW_WAIT = 1, 2, 4, 8
+FLAG_VERIFY_LEN, FLAG_ROW_OFFSETS, FLAG_NO_RESIDUAL, FLAG_WAIT = 1, 2, 4, 8
 LM_HEAD_ROWS, LM_HEAD_BLOCKED = 0, 1
 
 

@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
 // Each workgroup then waits for all C sums of its request, locates the draw exactly as
 // k_draw_finalize does, and the workgroup holding the hit chunk finishes the draw from
 // the weights still in its registers. The wait is bounded: a workgroup that has polled a
-// slot kDrawSpinLimit times raises SD_FLAG_DRAW_WAIT and writes -1, and the request's
+// slot kDrawSpinLimit times raises SD_FLAG_WAIT and writes -1, and the request's
 // token is then not valid.
 constexpr int kDrawOnePassMaxChunks = 256;
 constexpr int kDrawSpinLimit = 1 << 20;
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a) {
   __syncthreads();
   if (s_late) {
     if (tid == 0) {
-      raise_flag(a.ws, SD_FLAG_DRAW_WAIT);
+      raise_flag(a.ws, SD_FLAG_WAIT);
       a.next_token[r] = -1;
     }
     return;

@@ -16,7 +16,7 @@ static __device__ __align__(256) uint8_t scratch[SD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int kMaxGamma = 64;        // one wavefront of draft positions per request
 constexpr int kMaxVocab = 1 << 21;   // bound of the sampler's per-row tile table
 
@@ -58,13 +58,32 @@ hipError_t clear_words(void *p, int n, hipStream_t s) {
 
 __global__ void k_copy_word(const uint32_t *src, uint32_t *dst) { *dst = *src; }
 
+// Sets the publication area after a verify workspace's header to kPubEmpty words.
+__global__ void k_fill_pub(unsigned long long *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = kPubEmpty;
+}
+
+// A new workspace's header cleared and, when it is large enough to hold one, its
+// publication area emptied.
+hipError_t init_workspace(void *ws, size_t bytes, hipStream_t s) {
+  hipError_t e = clear_words(ws, sizeof(WsHeader) / 4, s);
+  if (e != hipSuccess || bytes < sizeof(WsHeader) + kPubBytes) return e;
+  const int n = 2 * kPubWords;
+  hipLaunchKernelGGL(k_fill_pub, dim3((n + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ws) + sizeof(WsHeader)), n);
+  return hipGetLastError();
+}
+
 // Device address of `scratch` on the current device, looked up on the first call made
 // with that device current and kept for the process.
 constexpr int kMaxScratchDevices = 256;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxScratchDevices] = {};
 
-hipError_t scratch_address(void **out) {
+// The first lookup on a device also prepares the scratch as sd_workspace_init prepares
+// a workspace (enqueued on s); the address is kept only once that is enqueued.
+hipError_t scratch_address(void **out, hipStream_t s) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -75,6 +94,8 @@ hipError_t scratch_address(void **out) {
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
+    e = init_workspace(p, SD_NOALLOC_SCRATCH_BYTES, s);
+    if (e != hipSuccess) return e;
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -113,7 +134,7 @@ size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
 int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
   if (!workspace || workspace_bytes < sizeof(WsHeader)) return SD_EWORKSPACE;
   if (!aligned(workspace, 256)) return SD_EALIGN;
-  return launch_status(clear_words(workspace, sizeof(WsHeader) / 4, (hipStream_t)stream));
+  return launch_status(init_workspace(workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 int32_t sd_device_flags(void *workspace, void *stream, uint32_t *flags, int32_t clear) {
@@ -336,15 +357,16 @@ int32_t sd_verify_greedy_noalloc(const uint16_t *hidden, const uint16_t *lm_head
                             B, gamma, d, V, 0.f, nullptr, stats, true, probe,
                             SD_NOALLOC_SCRATCH_BYTES, &a);
   if (st != SD_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
   void *ws = nullptr;
-  if (scratch_address(&ws) != hipSuccess) return SD_EDEVICE;
+  if (scratch_address(&ws, s) != hipSuccess) return SD_EDEVICE;
   st = verify_setup(hidden, lm_head, nullptr, false, draft_tokens, verify_len, row_offsets, B,
                     gamma, d, V, 0.f, nullptr, stats, true, ws, SD_NOALLOC_SCRATCH_BYTES, &a);
   if (st != SD_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  // The header (sticky flags, arrival ticket) starts every call at zero; partials and
-  // drafted-token logits are written in full by the contraction before they are read.
-  if (clear_words(ws, sizeof(WsHeader) / 4, s) != hipSuccess) return SD_EDEVICE;
+  // The flag word starts every call at zero. The rest of the header and the publication
+  // area carry over from the previous call, as in a workspace; partials and drafted-token
+  // logits are written in full by the contraction before they are read.
+  if (clear_words(ws, 1, s) != hipSuccess) return SD_EDEVICE;
   hipError_t e = launch_verify_greedy(a, accept_len, next_token, counters, s);
   if (e == hipSuccess && flags) {
     hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(1), 0, s, reinterpret_cast<const uint32_t *>(ws),

@@ -365,15 +365,68 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
   return part;
 }
 
+// Statistics of verified row j of request r (packed row m) once lane `lane` of the wave
+// holds its share (t1, t2, a1) of the row's merged partials: the wave reduces them, forms
+// the drafted token's exact logit when the contraction left none (zx NaN or absent), and
+// lane 0 writes the row's statistics and its argmax and drafted token to s_arg / s_x.
+// The merge is exact (max with lowest-id ties, and a max for the runner-up), so any
+// split of the partials over lanes gives the same bytes.
+// With write false nothing is written and no dot formed (a rehearsal on words that may
+// not all be final).
+__device__ inline void greedy_row_finish(const VerifyArgs &a, int r, int j, int L, int m, int x,
+                                         bool has_x, double zg, float t1, float t2, int a1,
+                                         int lane, int *s_arg, int *s_x, bool write = true) {
+  const bool need_dot = write && has_x && (!a.zx || zg != zg);
+  double part = 0.0;
+  if (need_dot)
+    part = lm_head_dot_part(a, a.hidden + ((size_t)r * (a.rm.gamma + 1) + j) * a.d, x, lane, 64);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+    const int oa = __shfl_xor(a1, off);
+    if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+    else { t2 = fmaxf(t2, o1); }
+    part += __shfl_xor(part, off);
+  }
+  if (write && lane == 0) {
+    sd_row_stats st;
+    st.argmax = a1;
+    st.top1 = t1;
+    st.top2 = t2;
+    st.pos = j;
+    st.lse = 0.0;
+    st.z_draft = need_dot ? part : (has_x ? zg : 0.0);
+    a.stats[m] = st;
+    s_arg[j] = a1;
+    if (j < L) s_x[j] = x;
+  }
+}
+
+// Greedy acceptance of request r from its rows' argmaxes in s_arg and drafted tokens in
+// s_x (LFM2.5-DSpark blog, "Quality parity"): a_r is the first row whose argmax differs
+// from the draft (L_r when none does) and the next token is that row's argmax. Wave 0.
+__device__ inline void greedy_decide(int r, int L, const int *s_arg, const int *s_x,
+                                     int32_t *accept_len, int32_t *next_token,
+                                     int64_t *counters, int lane) {
+  const bool miss = lane < L && s_arg[lane] != s_x[lane];
+  const unsigned long long mask = __ballot(miss);
+  const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
+  if (lane == 0) {
+    accept_len[r] = acc;
+    next_token[r] = s_arg[acc];
+    if (counters) {
+      atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
+      atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)acc);
+    }
+  }
+}
+
 // Greedy verify tail of request r, by the workgroup's nw waves (one wave per row):
 // merges the n partials of each of its rows 0..L_r, writes their statistics with the
-// drafted token's exact logit, then finds the first row whose argmax differs from the
-// draft and emits that row's argmax (LFM2.5-DSpark blog, "Quality parity"). s_arg[65]
-// and s_x[64] are LDS; every thread of the workgroup calls it, and it returns with the
-// workgroup converged (a request outside the row capacity returns early for all).
+// drafted token's exact logit, then decides. s_arg[65] and s_x[64] are LDS; every
+// thread of the workgroup calls it, and it returns with the workgroup converged (a
+// request outside the rows the contraction computed returns early for all).
 constexpr int kFusedPer = 8;    // loads in flight per lane
-// Requests up to which the streaming greedy verify decides inside the contraction's launch.
-constexpr int kGreedyTailMaxRequests = 2;
 
 __device__ inline void merge_accept_greedy_request(
     const VerifyArgs &a, int r, int n, int32_t *__restrict__ accept_len,
@@ -382,9 +435,8 @@ __device__ inline void merge_accept_greedy_request(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gamma = a.rm.gamma;
   const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
-  const int cap = a.rm.B * (gamma + 1);
   const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
-  if (base < 0 || base + L >= cap) {
+  if (base < 0 || base + L >= rows_total(a.rm)) {
     if (tid == 0) {
       raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
       accept_len[r] = 0;
@@ -417,43 +469,152 @@ __device__ inline void merge_accept_greedy_request(
         else { t2 = fmaxf(t2, q[i].top1); }
       }
     }
-    const bool need_dot = has_x && (!a.zx || zg != zg);
-    double part = 0.0;
-    if (need_dot)
-      part = lm_head_dot_part(a, a.hidden + ((size_t)r * (gamma + 1) + j) * a.d, x, lane, 64);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-      const int oa = __shfl_xor(a1, off);
-      if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-      else { t2 = fmaxf(t2, o1); }
-      part += __shfl_xor(part, off);
-    }
-    if (lane == 0) {
-      sd_row_stats st;
-      st.argmax = a1;
-      st.top1 = t1;
-      st.top2 = t2;
-      st.pos = j;
-      st.lse = 0.0;
-      st.z_draft = need_dot ? part : (has_x ? zg : 0.0);
-      a.stats[m] = st;
-      s_arg[j] = a1;
-      if (j < L) s_x[j] = x;
-    }
+    greedy_row_finish(a, r, j, L, m, x, has_x, zg, t1, t2, a1, lane, s_arg, s_x);
   }
   __syncthreads();
-  if (wave == 0) {
-    const bool miss = lane < L && s_arg[lane] != s_x[lane];
-    const unsigned long long mask = __ballot(miss);
-    const int acc = mask ? (__ffsll((long long)mask) - 1) : L;
-    if (lane == 0) {
-      accept_len[r] = acc;
-      next_token[r] = s_arg[acc];
-      if (counters) {
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters), (unsigned long long)L);
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 1), (unsigned long long)acc);
+  if (wave == 0) greedy_decide(r, L, s_arg, s_x, accept_len, next_token, counters, lane);
+}
+
+// ---------------------------------- greedy decision inside the streaming contraction
+// Words of a published partial: the bits of (top1, top2) and of (arg, sum). A partial's
+// arg is a vocabulary id or 0x7fffffff, never -1, so its second word is never kPubEmpty;
+// the first would need two fp32 NaNs with every bit set, which no arithmetic result
+// carries. A drafted-token logit is published as its fp64 bits: a computed value or a
+// quiet NaN from arithmetic, never all ones either.
+__device__ inline unsigned long long pub_word0(const TilePartial &p) {
+  return (unsigned long long)__float_as_uint(p.top1) |
+         ((unsigned long long)__float_as_uint(p.top2) << 32);
+}
+__device__ inline unsigned long long pub_word1(const TilePartial &p) {
+  return (unsigned long long)(uint32_t)p.arg | ((unsigned long long)__float_as_uint(p.sum) << 32);
+}
+__device__ inline void pub_store(unsigned long long *w, unsigned long long v) {
+  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned long long pub_load(unsigned long long *w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Buffer e & 1 of the publication area.
+__device__ inline unsigned long long *pub_buffer(const VerifyArgs &a, uint32_t e) {
+  return a.pub + (size_t)(e & 1u) * kPubWords;
+}
+// Layout of a launch with M rows and n contraction workgroups: partial (m, g) at words
+// 2 (m n + g) and 2 (m n + g) + 1, then the drafted-token logit of row m at 2 M n + m.
+__host__ __device__ inline int pub_words_used(int M, int n) { return 2 * M * n + M; }
+
+constexpr int kTailRowsPerWave = 3;                 // rows per wave: up to 12 per request
+constexpr int kTailMaxRows = 4 * kTailRowsPerWave;
+constexpr int kTailPerLane = kPubMaxGrid / 64;      // partials per lane and row
+constexpr int kTailMaxRequests = 16;
+constexpr int kTailSpinLimit = 1 << 20;
+
+// Greedy verify of request r inside the streaming contraction's launch, by a workgroup
+// appended to its grid; the n contraction workgroups publish every row's partial and
+// the drafted-token logits into buffer pub_epoch & 1. Wave w takes rows w, w + 4 and
+// w + 8 of the request, lane l the partials l + 64 i. The wave loads every word it needs,
+// and loads them again (after a short sleep) until none is kPubEmpty; each word is
+// written once per launch, so what it then holds is final. Rows are merged, finished and
+// decided exactly as merge_accept_greedy_request does. The last deciding workgroup to
+// finish (of B) records the words this launch published and moves the header to the
+// other buffer; every workgroup of the launch read the header before that. A wait that
+// runs out raises SD_FLAG_WAIT (the request's outputs are then not valid).
+__device__ void greedy_decide_published(const VerifyArgs &a, int r, int n, int *s_arg, int *s_x) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gamma = a.rm.gamma;
+  const uint32_t epoch = a.ws->pub_epoch;
+  unsigned long long *buf = pub_buffer(a, epoch);
+  const int M = rows_total(a.rm);
+  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
+  if (base < 0 || base + L >= M) {
+    if (tid == 0) {
+      raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+      a.greedy_accept_len[r] = 0;
+      a.greedy_next_token[r] = -1;
+    }
+  } else {
+    const int ipr = (n + 63) / 64;
+    // zx[k]: whether the contraction publishes row k's drafted-token logit. It does for
+    // a drafted row when it maps that packed row back to this request and position;
+    // offsets that disagree with the lengths make it map the row elsewhere, and the
+    // row then takes the fp64 dot here (flagged).
+    int x[kTailRowsPerWave];
+    bool hx[kTailRowsPerWave], zx[kTailRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kTailRowsPerWave; ++k) {
+      const int j = wave + 4 * k;
+      x[k] = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
+      hx[k] = x[k] >= 0 && x[k] < a.V;
+      int rq = -1, jj = -1;
+      if (hx[k]) hidden_row(a.rm, base + j, &rq, &jj);
+      zx[k] = hx[k] && rq == r && jj == j;
+      if (hx[k] && !zx[k] && lane == 0) raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
+    }
+    unsigned long long w0[kTailRowsPerWave][kTailPerLane], w1[kTailRowsPerWave][kTailPerLane];
+    unsigned long long zw[kTailRowsPerWave];
+    for (int it = 0;; ++it) {
+      // Every load is issued before any is tested. Rows past L_r, partials past n and
+      // rows without a published logit load a word the request does publish (row L_r,
+      // partial n - 1) and are left out of the merge.
+#pragma unroll
+      for (int k = 0; k < kTailRowsPerWave; ++k) {
+        const size_t row = (size_t)(base + min(wave + 4 * k, L)) * n;
+#pragma unroll
+        for (int i = 0; i < kTailPerLane; ++i) {
+          unsigned long long *w = buf + 2 * (row + min(lane + 64 * i, n - 1));
+          w0[k][i] = pub_load(w);
+          w1[k][i] = pub_load(w + 1);
+        }
+        zw[k] = pub_load(zx[k] ? buf + 2 * (size_t)M * n + base + wave + 4 * k : buf + 2 * row);
       }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < kTailRowsPerWave; ++k) {
+#pragma unroll
+        for (int i = 0; i < kTailPerLane; ++i)
+          ok &= (w0[k][i] != kPubEmpty) & (w1[k][i] != kPubEmpty);
+        ok &= zw[k] != kPubEmpty;
+      }
+      const bool all_ok = __all(ok);
+      const bool last = all_ok || it == kTailSpinLimit;
+      if (last && !all_ok && lane == 0) raise_flag(a.ws, SD_FLAG_WAIT);
+      // The rows are merged and finished on every round, written only on the last: the
+      // last round then runs code the wave has just run.
+#pragma unroll
+      for (int k = 0; k < kTailRowsPerWave; ++k) {
+        const int j = wave + 4 * k;
+        if (j > L) break;
+        float t1 = -INFINITY, t2 = -INFINITY;
+        int a1 = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kTailPerLane; ++i) {
+          if (i < ipr && lane + 64 * i < n) {
+            const float q1 = __uint_as_float((uint32_t)w0[k][i]);
+            const float q2 = __uint_as_float((uint32_t)(w0[k][i] >> 32));
+            const int qa = (int)(uint32_t)w1[k][i];
+            if (beats(q1, qa, t1, a1)) { t2 = fmaxf(t1, q2); t1 = q1; a1 = qa; }
+            else { t2 = fmaxf(t2, q1); }
+          }
+        }
+        const double zg = zx[k] ? __longlong_as_double((long long)zw[k])
+                        : hx[k] ? __longlong_as_double(0x7ff8000000000000ll) : 0.0;
+        greedy_row_finish(a, r, j, L, base + j, x[k], hx[k], zg, t1, t2, a1, lane, s_arg, s_x,
+                          last);
+      }
+      if (last) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+    if (wave == 0)
+      greedy_decide(r, L, s_arg, s_x, a.greedy_accept_len, a.greedy_next_token,
+                    a.greedy_counters, lane);
+  }
+  if (tid == 0) {
+    const uint32_t done = a.rm.B == 1 ? 0u : atomicAdd(&a.ws->pub_done, 1u);
+    if (done == (uint32_t)(a.rm.B - 1)) {
+      a.ws->pub_done = 0u;
+      a.ws->pub_prev = (uint32_t)pub_words_used(M, n);
+      a.ws->pub_epoch = epoch + 1u;
     }
   }
 }
@@ -531,10 +692,22 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     draft_partials_walk(a, (int)blockIdx.x - a.g_main, (int)gridDim.x - a.g_main);
     return;
   }
+  // With a publication area, workgroups past the grid decide greedy acceptance, one
+  // request each, from what the contraction's workgroups publish.
+  if (a.pub && (int)blockIdx.x >= a.g_main) {
+    int *s_i = reinterpret_cast<int *>(S);
+    greedy_decide_published(a, (int)blockIdx.x - a.g_main, a.g_main, s_i, s_i + 72);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.g_main, g = blockIdx.x;
   const int M = rows_total(a.rm);
   const int d = a.d, V = a.V;
+  // Publication buffer of this launch, and the words the previous publishing launch left
+  // in the other one (this launch returns them to kPubEmpty).
+  const uint32_t pub_epoch = a.pub ? a.ws->pub_epoch : 0u;
+  const uint32_t pub_prev = a.pub ? a.ws->pub_prev : 0u;
+  unsigned long long *const pbuf = a.pub ? pub_buffer(a, pub_epoch) : nullptr;
 
   // LM-head load i of this thread: bf16 rows r = RPI * (wave + 4 i) + lane / CH, stored
   // chunk lane % CH (swizzled); W12 16-byte piece u = 64 (wave + 4 i) + lane of the
@@ -781,12 +954,19 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
         }
 #pragma unroll
         for (int off = CH / 2; off >= 1; off >>= 1) zacc += __shfl_xor(zacc, off);
-        if (lane == 0) a.zx[zrow] = zacc;
+        if (lane == 0) {
+          if (pbuf) pub_store(pbuf + 2 * (size_t)M * G + zrow, (unsigned long long)__double_as_longlong(zacc));
+          else a.zx[zrow] = zacc;
+        }
       }
       if (tid == 0 && zmask) {
         unsigned long long mm = zmask;
         for (int i = 0; i < 4 && mm; ++i) mm &= mm - 1;
-        for (; mm; mm &= mm - 1) a.zx[__ffsll((long long)mm) - 1] = __longlong_as_double(0x7ff8000000000000ll);
+        for (; mm; mm &= mm - 1) {
+          const int zr = __ffsll((long long)mm) - 1;
+          if (pbuf) pub_store(pbuf + 2 * (size_t)M * G + zr, 0x7ff8000000000000ull);
+          else a.zx[zr] = __longlong_as_double(0x7ff8000000000000ll);
+        }
       }
       zrow = -1;
     }
@@ -807,28 +987,19 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(VerifyArgs a, int kstride) 
     for (int w = 1; w < 4; ++w) row_acc_merge(r0, X[w * 16 * MT + tid], a.scale_log2);
     TilePartial p;
     p.top1 = r0.t1; p.top2 = r0.t2; p.arg = r0.arg; p.sum = r0.sum;
-    a.partials[(size_t)tid * a.part_stride + g] = p;
+    if (pbuf) {
+      unsigned long long *w = pbuf + 2 * ((size_t)tid * G + g);
+      pub_store(w, pub_word0(p));
+      pub_store(w + 1, pub_word1(p));
+    } else {
+      a.partials[(size_t)tid * a.part_stride + g] = p;
+    }
   }
-  if (!a.greedy_accept_len) return;
-
-  // Greedy verify tail in this launch (no second kernel). Each workgroup makes its
-  // partials and drafted-token logits visible device-wide, then takes a ticket; the
-  // workgroup that draws the last one merges every request's rows and decides, exactly
-  // as k_merge_accept_greedy does, and returns the ticket counter to zero for the next
-  // launch. No workgroup waits for another.
-  __threadfence();
-  __syncthreads();
-  int *s_i = reinterpret_cast<int *>(S);
-  if (tid == 0) s_i[0] = atomicAdd(&a.ws->ticket, 1u) == (unsigned)(G - 1);
-  __syncthreads();
-  if (!s_i[0]) return;
-  __threadfence();
-  for (int r = 0; r < a.rm.B; ++r) {
-    merge_accept_greedy_request(a, r, G, a.greedy_accept_len, a.greedy_next_token,
-                                a.greedy_counters, 4, s_i + 4, s_i + 72);
-    __syncthreads();   // s_arg and s_x are rewritten by the next request
+  if (pbuf) {
+    unsigned long long *other = pub_buffer(a, pub_epoch + 1u);
+    for (uint32_t w = (uint32_t)g * 256u + tid; w < pub_prev; w += (uint32_t)G * 256u)
+      pub_store(other + w, kPubEmpty);
   }
-  if (tid == 0) a.ws->ticket = 0u;
 }
 
 // ----------------------------------------------------------------- tiled regime
@@ -1539,7 +1710,8 @@ struct Occupancy {
 };
 thread_local Occupancy t_occ;
 
-int resident_blocks(const void *fn) {
+// Compute units of the current device.
+int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (t_occ.device != dev) {
@@ -1550,6 +1722,11 @@ int resident_blocks(const void *fn) {
     t_occ.cus = cus > 0 ? cus : 1;
     t_occ.device = dev;
   }
+  return t_occ.cus;
+}
+
+int resident_blocks(const void *fn) {
+  device_cus();
   int slot = 0;
   while (slot < 16 && t_occ.fn[slot] && t_occ.fn[slot] != fn) ++slot;
   if (slot < 16 && t_occ.fn[slot] == fn) return t_occ.cus * t_occ.per_cu[slot];
@@ -1587,12 +1764,6 @@ int stage_stride(int nst) {
   return 1;
 }
 
-// The greedy tail inside the streaming contraction pays a device-scope release fence
-// per workgroup and merges in one 4-wave workgroup; it beats a separate merge launch only
-// on small grids (measured: a 16-workgroup grid's step 17.5 -> 10.8 us, a 512-workgroup
-// grid's 28 -> 98 us).
-constexpr int kGreedyTailMaxGrid = 32;
-
 // Drafter-normaliser workgroups appended to a streaming contraction of G workgroups out of
 // `resident` slots: the idle slots, up to one workgroup per four (row, chunk) items, and
 // none unless every wave then takes at most kDraftItemsPerWave items (otherwise the
@@ -1615,12 +1786,25 @@ hipError_t launch_skinny_as(const VerifyArgs &a, hipStream_t stream, int *n_part
   *n_part = G;
   VerifyArgs k = a;
   k.g_main = G;
-  const bool tail = a.greedy_accept_len && G <= kGreedyTailMaxGrid;
-  if (!tail) k.greedy_accept_len = nullptr;
+  // The greedy decision joins this launch when one deciding workgroup per request can
+  // take its request's rows in one pass, the publication area holds the launch, and the
+  // deciding workgroups get compute units of their own. Workgroups go out one per CU
+  // before any CU takes a second; a decider that shares its CU with a streaming
+  // workgroup waits behind that workgroup's loads (measured on a 512-workgroup grid:
+  // 2-3 us per poll, a slower step than the separate launch).
+  const int cap = a.rm.B * (a.rm.gamma + 1);
+  const bool tail = a.pub && a.greedy_accept_len && a.rm.B <= kTailMaxRequests &&
+                    a.rm.gamma + 1 <= kTailMaxRows && G + a.rm.B <= device_cus() &&
+                    G <= kPubMaxGrid && pub_words_used(cap, G) <= kPubWords;
+  if (!tail) {
+    k.pub = nullptr;
+    k.greedy_accept_len = nullptr;
+  }
   if (greedy_done) *greedy_done = tail;
-  const int extra = a.dpart && a.draft_logits ? appended_draft_grid(a, G, resident) : 0;
-  if (!extra) k.dpart = nullptr;
-  if (draft_done) *draft_done = extra > 0;
+  const int extra = tail ? a.rm.B
+                  : a.dpart && a.draft_logits ? appended_draft_grid(a, G, resident) : 0;
+  if (tail || !extra) k.dpart = nullptr;
+  if (draft_done) *draft_done = !tail && extra > 0;
   hipLaunchKernelGGL((k_gemm_skinny<MT, KC, NS, FMT>), dim3(G + extra), dim3(256), 0, stream, k,
                      stage_stride(a.d / KC));
   return hipGetLastError();
@@ -1673,7 +1857,7 @@ size_t verify_workspace_layout(int B, int gamma, int V, size_t *part_off, int *p
                                size_t *zx_off) {
   const size_t cap = (size_t)B * (gamma + 1);
   const int stride = (V + kMinVocabTile - 1) / kMinVocabTile;
-  const size_t po = sizeof(WsHeader);
+  const size_t po = sizeof(WsHeader) + kPubBytes;   // header, publication area, partials
   const size_t zo = po + align_up(cap * (size_t)stride * sizeof(TilePartial), 256);
   if (part_off) *part_off = po;
   if (part_stride) *part_stride = stride;
@@ -1719,10 +1903,12 @@ hipError_t launch_contraction(const VerifyArgs &a, hipStream_t stream, int *n_pa
 
 hipError_t launch_verify_greedy(const VerifyArgs &a, int32_t *accept_len, int32_t *next_token,
                                 int64_t *counters, hipStream_t stream) {
-  // A small streaming contraction with few requests finishes the step in its own launch
-  // (its last workgroup merges and decides); otherwise a separate launch does that.
+  // A streaming contraction with few requests of few rows finishes the step in its own
+  // launch (workgroups appended to its grid decide, from partials published in the
+  // workspace's publication area); otherwise a separate launch does that.
   VerifyArgs f = a;
-  if (a.rm.B <= kGreedyTailMaxRequests && a.zx && a.draft_tokens) {
+  if (a.zx && a.draft_tokens) {
+    f.pub = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(a.ws) + sizeof(WsHeader));
     f.greedy_accept_len = accept_len;
     f.greedy_next_token = next_token;
     f.greedy_counters = counters;

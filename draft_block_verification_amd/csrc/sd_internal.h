@@ -19,10 +19,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Workspace header: a 256-byte block at the start of every workspace.
 struct WsHeader {
   uint32_t flags;      // sticky SD_FLAG_* bits
-  uint32_t ticket;     // arrival counter for last-workgroup epilogues (returns to 0)
-  uint32_t pad[62];
+  // Publication area state of the in-launch greedy decision (verify workspaces):
+  uint32_t pub_done;   // deciding workgroups finished in the running launch (returns to 0)
+  uint32_t pub_epoch;  // launches that published; buffer pub_epoch & 1 is the next one's
+  uint32_t pub_prev;   // words the last of them published into its buffer
+  uint32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+// Publication area of a verify workspace (right after its header): two buffers of
+// kPubWords 64-bit words that a streaming contraction's workgroups publish their row
+// partials and drafted-token logits into, with device-scope atomic stores, for the
+// workgroups appended to the same launch that merge them and decide greedy acceptance.
+// A word that holds kPubEmpty has not been published in the running launch. Launches
+// alternate buffers; each one returns the other buffer's published words to kPubEmpty,
+// so a buffer is empty whenever a launch starts on it. Holds 64 rows x 512 workgroups
+// (two words per partial) and 64 drafted-token logits.
+constexpr int kPubMaxGrid = 512;
+constexpr int kPubWords = 2 * 64 * kPubMaxGrid + 64;
+constexpr size_t kPubBytes = 2 * (size_t)kPubWords * 8;
+constexpr unsigned long long kPubEmpty = ~0ull;
 
 // Statistics of one verified row over one vocabulary tile.
 struct TilePartial {
@@ -178,9 +194,11 @@ struct VerifyArgs {
   // Blocked bf16 LM head: W holds [d/128][ceil(V/64)][64][128] (stage-major), row r's
   // 16-byte chunk j of a block at position j ^ (r & 15), rows past V zero.
   bool w_blocked;
-  // Greedy verify decided inside the streaming contraction's launch: when
-  // greedy_accept_len is set, its last workgroup writes the statistics and these outputs
-  // (counters may be null). Uses the workspace header's ticket word.
+  // Greedy verify decided inside the streaming contraction's launch: with pub set (the
+  // workspace's publication area), workgroups g_main .. g_main + B - 1 appended to the
+  // grid merge request r = g - g_main's published partials and write its statistics and
+  // these outputs (counters may be null).
+  unsigned long long *pub;
   int32_t *greedy_accept_len;
   int32_t *greedy_next_token;
   int64_t *greedy_counters;

@@ -78,9 +78,10 @@ enum {
     SD_FLAG_VERIFY_LEN = 1,   /* a verify_len entry was outside [0, gamma] and was clamped */
     SD_FLAG_ROW_OFFSETS = 2,  /* row_offsets disagreed with verify_len or overflowed the row capacity */
     SD_FLAG_NO_RESIDUAL = 4,  /* a residual max(0, p - q) had no positive mass; drew from p instead */
-    SD_FLAG_DRAW_WAIT = 8     /* sd_verify_rejection's one-launch draw waited too long for its
-                                 other workgroups (they could not all run at once); the
-                                 tokens of that call are not valid */
+    SD_FLAG_WAIT = 8          /* a workgroup's bounded wait for results that other workgroups
+                                 of the same launch publish ran out (sd_verify_rejection's
+                                 one-launch draw, sd_verify_greedy's in-launch decision);
+                                 the tokens of that call are not valid */
 };
 
 /* Per verified row statistics (32 bytes, 8-byte aligned). */
@@ -106,7 +107,10 @@ SD_API size_t sd_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t d, int
 /* Workspace bytes sd_accept_rejection needs for these sizes (0 on invalid sizes). */
 SD_API size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
 
-/* Prepare a freshly allocated workspace (clears its flag word and counters).
+/* Prepare a freshly allocated workspace: clears its 256-byte header (flag word and
+ * counters) and, in a workspace of more than 256 + 2 * 525 KiB bytes (every verify
+ * workspace), sets the publication area that follows the header to all ones bytes (the
+ * state sd_verify_greedy's in-launch decision expects; every later call leaves it so).
  * Must be called once per workspace before its first use; enqueued on `stream`. */
 SD_API int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
@@ -206,9 +210,11 @@ SD_API int32_t sd_verify_contraction(const uint16_t *hidden, const uint16_t *lm_
  * Greedy verify of a drafted block in one call (LFM2.5-DSpark blog, "How DSpark
  * works" and "Quality parity"): the LM-head contraction at temperature 0 followed
  * by one kernel that merges each request's row statistics and decides acceptance.
- * When the streaming contraction runs on a grid of at most 32 workgroups for at most
- * 2 requests, its last workgroup merges and decides instead (no second launch); that
- * uses the workspace header's ticket word, which every call leaves at zero.
+ * When the streaming contraction runs (B * (gamma + 1) <= 64, d % 128 == 0) for at most
+ * 16 requests of at most 12 rows (gamma <= 11) on a grid that leaves a compute unit for
+ * each request (up to about V = 16000 on MI355X), workgroups appended to its launch merge
+ * and decide instead (no second launch): the contraction's workgroups publish their row
+ * partials in the workspace's publication area, which the call leaves as it found it.
  * Outputs are the same bytes as sd_verify_logits (temperature 0, logits NULL)
  * followed by sd_accept_greedy, with one or two launches fewer.
  *   hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma, d, V

@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sd.abi_version() == 1
+    assert sd.abi_version() == 2
     lib.sd_status_string.restype = ctypes.c_char_p
     assert lib.sd_status_string(0) == b"ok"
     assert b"workspace" in lib.sd_status_string(4)
@@ -42,10 +42,12 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_sizes():
-    # Header, then one 16-byte partial per (row, 64-wide vocabulary tile).
+    # Header; the publication area (two buffers of 2 * 64 * 512 + 64 words); one 16-byte
+    # partial per (row, 64-wide vocabulary tile); fp64 drafted-token logits.
     up = lambda x: (x + 255) // 256 * 256
+    pub = 2 * (2 * 64 * 512 + 64) * 8
     b = sd.verify_workspace_bytes(1, 9, 2048, 32768)
-    assert b == 256 + up(10 * 512 * 16) + up(10 * 8)   # partials, then fp64 drafted-token logits
+    assert b == 256 + pub + up(10 * 512 * 16) + up(10 * 8)
     assert sd.verify_workspace_bytes(32, 16, 4096, 151936) >= 32 * 17 * (151936 // 64) * 16
     assert sd.accept_workspace_bytes(128, 16, 129280) >= 256 + 128 * 16 * 8 + 128 * 16 * 32 * 16
     for bad in [(0, 9, 2048, 100), (1, 0, 2048, 100), (1, 65, 2048, 100), (1, 4, 12, 100),

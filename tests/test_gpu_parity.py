@@ -210,12 +210,19 @@ def test_determinism_bytes():
     ("fused-tiled", dict(B=20, gamma=8, d=128, V=5000, truncate=True)),
     ("fused-gamma64", dict(B=2, gamma=64, d=64, V=700)),
     ("fused-many", dict(B=300, gamma=3, d=64, V=129, truncate=True)),
-    # Streaming grids of at most 32 workgroups with at most 2 requests decide inside the
-    # contraction's launch (its last workgroup merges); 2048 ids = 32 slabs of 64.
+    # Streaming contractions of at most 16 requests of at most 12 rows, whose grid leaves
+    # a compute unit per request, decide inside the contraction's launch (workgroups
+    # appended to its grid merge published partials); greedy-block9 (512 workgroups) and
+    # the last three take the separate launch.
     ("tail-tiny", dict(B=1, gamma=4, d=256, V=1024)),
     ("tail-32-trunc", dict(B=2, gamma=9, d=384, V=2048, truncate=True)),
     ("tail-blocked", dict(B=2, gamma=7, d=256, V=1500, blocked=True)),
-    ("tail-33-separate", dict(B=1, gamma=9, d=256, V=2049)),
+    ("tail-33-slabs", dict(B=1, gamma=9, d=256, V=2049)),
+    ("tail-16-requests", dict(B=16, gamma=3, d=256, V=5000, truncate=True)),
+    ("tail-12-rows-188-slabs", dict(B=4, gamma=11, d=128, V=12000)),
+    ("tail-13-rows-separate", dict(B=4, gamma=12, d=128, V=7000)),
+    ("tail-17-requests-separate", dict(B=17, gamma=2, d=128, V=7000)),
+    ("tail-512-grid-separate", dict(B=4, gamma=11, d=128, V=70000)),
 ], ids=lambda c: c[0])
 def test_fused_greedy_matches_separate_calls(case):
     """sd_verify_greedy writes the same bytes as sd_verify_logits + sd_accept_greedy."""
@@ -243,6 +250,46 @@ def test_fused_greedy_matches_separate_calls(case):
             assert sd.device_flags(vr.ws_verify) == 0
         for a, b in zip(*outs):
             assert torch.equal(a, b)
+
+
+def test_in_launch_decision_across_shapes_on_one_workspace():
+    """One verify workspace serves greedy calls of changing shapes (grids of 16 to 512
+    workgroups, 4 to 64 rows, truncated and not, deciding in the launch or not), with
+    sd_verify_logits calls on it in between. The in-launch decision relies on the
+    workspace's publication area being empty whenever a launch starts on it, so every
+    call must equal the two-call path."""
+    shapes = [dict(B=1, gamma=9, d=256, V=14000), dict(B=3, gamma=5, d=128, V=3001, truncate=True),
+              dict(B=16, gamma=3, d=256, V=1000), dict(B=1, gamma=11, d=128, V=16000, truncate=True),
+              dict(B=1, gamma=4, d=256, V=1024), dict(B=1, gamma=9, d=256, V=32768)]
+    ws = sd.new_workspace(max(sd.verify_workspace_bytes(sh["B"], sh["gamma"], sh["d"], sh["V"])
+                              for sh in shapes), "cuda")
+    heads = {}
+    for i, k in enumerate([0, 1, 2, 0, 3, 5, 1, 4, 0, 2, 5, 3, 3, 4, 0]):
+        w = workload("ragged-b32", T=0.0, name=f"seq{k}", **shapes[k])
+        if k not in heads:
+            W = make_weights(w)
+            heads[k] = (W, bf16_dev(W))
+        W, W_dev = heads[k]
+        say("sequence", i, shapes[k])
+        ds = upload_step(make_step(w, W, i))
+        vlen = offs = None
+        if w.truncate:
+            vlen, offs = sd.sd_truncate_by_confidence(ds.conf, w.threshold)
+        M = int(offs[-1].item()) if w.truncate else w.B * (w.gamma + 1)
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        st_f, acc_f, nxt_f = sd.sd_verify_greedy(ds.hidden, W_dev, ds.draft_tokens, vlen, offs,
+                                                 counters=cnt, workspace=ws)
+        _, st_s = sd.sd_verify_logits(ds.hidden, W_dev, ds.draft_tokens, vlen, offs, 0.0)
+        cnt_s = torch.zeros(2, dtype=torch.int64, device="cuda")
+        acc_s, nxt_s = sd.sd_accept_greedy(st_s, ds.draft_tokens, vlen, offs, counters=cnt_s)
+        if i % 3 == 2:
+            # A plain verify on the shared workspace: row partials, not the publication area.
+            sd.sd_verify_logits(ds.hidden, W_dev, ds.draft_tokens, vlen, offs, 0.0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(st_f[:M], st_s[:M])
+        assert torch.equal(acc_f, acc_s) and torch.equal(nxt_f, nxt_s)
+        assert torch.equal(cnt, cnt_s)
+    assert sd.device_flags(ws) == 0
 
 
 REJ_FUSED = [
