@@ -434,9 +434,13 @@ __device__ inline void merge_accept_greedy_request(
     int *s_x) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gamma = a.rm.gamma;
-  const int L = clamp_len(a.verify_len, r, gamma, tid == 0 ? a.ws : nullptr);
+  // Two rounds of loads: the request's length, offset and the row count together, then
+  // each row's drafted token, drafted-token logit and partials together.
+  const int Lraw = a.verify_len ? a.verify_len[r] : gamma;
   const int base = a.rm.row_offsets ? a.rm.row_offsets[r] : r * (gamma + 1);
-  if (base < 0 || base + L >= rows_total(a.rm)) {
+  const int M = rows_total(a.rm);
+  const int L = clamp_len_value(Lraw, gamma, tid == 0 ? a.ws : nullptr);
+  if (base < 0 || base + L >= M) {
     if (tid == 0) {
       raise_flag(a.ws, SD_FLAG_ROW_OFFSETS);
       accept_len[r] = 0;
@@ -446,13 +450,13 @@ __device__ inline void merge_accept_greedy_request(
   }
   for (int j = wave; j <= L; j += nw) {
     const int m = base + j;
-    // The drafted token, its logit from the contraction when that left one, and the
-    // partials are loaded together; only without a logit (NaN or none) are the hidden
-    // and LM-head rows read for the fp64 dot.
-    const int x = j < L ? a.draft_tokens[(size_t)r * gamma + j] : -1;
+    // Only without a logit from the contraction (NaN or none) are the hidden and LM-head
+    // rows read for the fp64 dot.
+    const int xr = j < gamma ? a.draft_tokens[(size_t)r * gamma + j] : -1;
+    const double zr = a.zx ? a.zx[m] : 0.0;
+    const int x = j < L ? xr : -1;
     const bool has_x = x >= 0 && x < a.V;
-    double zg = 0.0;
-    if (has_x && a.zx) zg = a.zx[m];
+    const double zg = has_x ? zr : 0.0;
     const TilePartial *P = a.partials + (size_t)m * a.part_stride;
     float t1 = -INFINITY, t2 = -INFINITY;
     int a1 = 0x7fffffff;

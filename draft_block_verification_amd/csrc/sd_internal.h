@@ -125,15 +125,19 @@ __device__ inline void raise_flag(WsHeader *ws, uint32_t bit) {
   if (ws) atomicOr(&ws->flags, bit);
 }
 
-// Kept drafts of request r, clamped to [0, gamma] (flagged when out of range).
-__device__ inline int clamp_len(const int32_t *verify_len, int r, int gamma, WsHeader *ws) {
-  if (!verify_len) return gamma;
-  int L = verify_len[r];
+// A kept-draft count clamped to [0, gamma] (flagged when out of range).
+__device__ inline int clamp_len_value(int L, int gamma, WsHeader *ws) {
   if (L < 0 || L > gamma) {
     raise_flag(ws, SD_FLAG_VERIFY_LEN);
     L = L < 0 ? 0 : gamma;
   }
   return L;
+}
+
+// Kept drafts of request r, clamped to [0, gamma] (flagged when out of range).
+__device__ inline int clamp_len(const int32_t *verify_len, int r, int gamma, WsHeader *ws) {
+  if (!verify_len) return gamma;
+  return clamp_len_value(verify_len[r], gamma, ws);
 }
 
 // fp64 sum of h[k] * w[k] over eight bf16 pairs (every product is exact in fp64).
