@@ -74,6 +74,43 @@ __device__ inline double lane_xor(double x, int off) {
   return __longlong_as_double((long long)(lo | (hi << 32)));
 }
 
+// Lane i's value from lane i ^ 1 or i ^ 2 (quad permutes), or from lane (i + 4) or
+// (i + 8) mod 16 of its row (row rotations): cross-lane moves in the VALU, no LDS.
+__device__ inline uint32_t lane_dpp_u32(uint32_t x, int ctrl) {
+  switch (ctrl) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+  }
+}
+
+// Merge of disjoint sets' (max, runner-up, lowest id of the max): every lane of the wave
+// ends with the triple of all 64 lanes. Quad permutes, then row rotations by 4 and 8
+// (after the quads, lane i and lane i + 4 of a row hold different quads, then different
+// halves), then the 16- and 32-lane swaps; every step merges two disjoint sets, and the
+// merge is exact, so the result is the same triple whatever the order.
+__device__ inline void wave_merge_top2(float &t1, float &t2, int &a1) {
+#pragma unroll
+  for (int step = 0; step < 6; ++step) {
+    float o1, o2;
+    int oa;
+    if (step < 4) {
+      const int c = 1 << step;
+      o1 = __uint_as_float(lane_dpp_u32(__float_as_uint(t1), c));
+      o2 = __uint_as_float(lane_dpp_u32(__float_as_uint(t2), c));
+      oa = (int)lane_dpp_u32((uint32_t)a1, c);
+    } else {
+      const int off = step == 4 ? 16 : 32;
+      o1 = lane_xor(t1, off);
+      o2 = lane_xor(t2, off);
+      oa = lane_xor(a1, off);
+    }
+    if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
+    else { t2 = fmaxf(t2, o1); }
+  }
+}
+
 // Fold a tile's (t1, t2, arg, sum) into a running value; sums are relative to t1.
 __device__ inline void row_acc_merge(RowAcc &r, const RowAcc &o, float scale_log2) {
   const bool win = beats(o.t1, o.arg, r.t1, r.arg);
@@ -371,24 +408,18 @@ __device__ inline double lm_head_dot_part(const VerifyArgs &a, const uint16_t *h
 // lane 0 writes the row's statistics and its argmax and drafted token to s_arg / s_x.
 // The merge is exact (max with lowest-id ties, and a max for the runner-up), so any
 // split of the partials over lanes gives the same bytes.
-// With write false nothing is written and no dot formed (a rehearsal on words that may
-// not all be final).
 __device__ inline void greedy_row_finish(const VerifyArgs &a, int r, int j, int L, int m, int x,
                                          bool has_x, double zg, float t1, float t2, int a1,
-                                         int lane, int *s_arg, int *s_x, bool write = true) {
-  const bool need_dot = write && has_x && (!a.zx || zg != zg);
+                                         int lane, int *s_arg, int *s_x) {
+  const bool need_dot = has_x && (!a.zx || zg != zg);
   double part = 0.0;
-  if (need_dot)
+  if (need_dot) {
     part = lm_head_dot_part(a, a.hidden + ((size_t)r * (a.rm.gamma + 1) + j) * a.d, x, lane, 64);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
-    const int oa = __shfl_xor(a1, off);
-    if (beats(o1, oa, t1, a1)) { t2 = fmaxf(t1, o2); t1 = o1; a1 = oa; }
-    else { t2 = fmaxf(t2, o1); }
-    part += __shfl_xor(part, off);
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
   }
-  if (write && lane == 0) {
+  wave_merge_top2(t1, t2, a1);
+  if (lane == 0) {
     sd_row_stats st;
     st.argmax = a1;
     st.top1 = t1;
@@ -579,34 +610,32 @@ __device__ void greedy_decide_published(const VerifyArgs &a, int r, int n, int *
           ok &= (w0[k][i] != kPubEmpty) & (w1[k][i] != kPubEmpty);
         ok &= zw[k] != kPubEmpty;
       }
-      const bool all_ok = __all(ok);
-      const bool last = all_ok || it == kTailSpinLimit;
-      if (last && !all_ok && lane == 0) raise_flag(a.ws, SD_FLAG_WAIT);
-      // The rows are merged and finished on every round, written only on the last: the
-      // last round then runs code the wave has just run.
-#pragma unroll
-      for (int k = 0; k < kTailRowsPerWave; ++k) {
-        const int j = wave + 4 * k;
-        if (j > L) break;
-        float t1 = -INFINITY, t2 = -INFINITY;
-        int a1 = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kTailPerLane; ++i) {
-          if (i < ipr && lane + 64 * i < n) {
-            const float q1 = __uint_as_float((uint32_t)w0[k][i]);
-            const float q2 = __uint_as_float((uint32_t)(w0[k][i] >> 32));
-            const int qa = (int)(uint32_t)w1[k][i];
-            if (beats(q1, qa, t1, a1)) { t2 = fmaxf(t1, q2); t1 = q1; a1 = qa; }
-            else { t2 = fmaxf(t2, q1); }
-          }
-        }
-        const double zg = zx[k] ? __longlong_as_double((long long)zw[k])
-                        : hx[k] ? __longlong_as_double(0x7ff8000000000000ll) : 0.0;
-        greedy_row_finish(a, r, j, L, base + j, x[k], hx[k], zg, t1, t2, a1, lane, s_arg, s_x,
-                          last);
+      if (__all(ok)) break;
+      if (it == kTailSpinLimit) {
+        if (lane == 0) raise_flag(a.ws, SD_FLAG_WAIT);
+        break;
       }
-      if (last) break;
       __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int k = 0; k < kTailRowsPerWave; ++k) {
+      const int j = wave + 4 * k;
+      if (j > L) break;
+      float t1 = -INFINITY, t2 = -INFINITY;
+      int a1 = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < kTailPerLane; ++i) {
+        if (i < ipr && lane + 64 * i < n) {
+          const float q1 = __uint_as_float((uint32_t)w0[k][i]);
+          const float q2 = __uint_as_float((uint32_t)(w0[k][i] >> 32));
+          const int qa = (int)(uint32_t)w1[k][i];
+          if (beats(q1, qa, t1, a1)) { t2 = fmaxf(t1, q2); t1 = q1; a1 = qa; }
+          else { t2 = fmaxf(t2, q1); }
+        }
+      }
+      const double zg = zx[k] ? __longlong_as_double((long long)zw[k])
+                      : hx[k] ? __longlong_as_double(0x7ff8000000000000ll) : 0.0;
+      greedy_row_finish(a, r, j, L, base + j, x[k], hx[k], zg, t1, t2, a1, lane, s_arg, s_x);
     }
     __syncthreads();
     if (wave == 0)
