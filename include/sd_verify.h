@@ -242,8 +242,9 @@ SD_API int32_t sd_verify_greedy(const uint16_t *hidden, const uint16_t *lm_head,
  *   hidden, lm_head, draft_tokens, verify_len, row_offsets, B, gamma, d, V, stats,
  *   accept_len, next_token, counters   as for sd_verify_greedy (bf16 [V][d] LM head)
  *   flags   device uint32 [1] out, 4-byte aligned, or NULL: this call's sticky device
- *           flag word (SD_FLAG_*); the scratch header is cleared at the start of every
- *           call, so flags cover this call only
+ *           flag word (SD_FLAG_*); the scratch's flag word is cleared at the start of
+ *           every call, so flags cover this call only (the first call on a device also
+ *           prepares the scratch as sd_workspace_init prepares a workspace)
  *   stream  hipStream_t of the device that is current at the call
  * Limit: sd_verify_workspace_bytes(B, gamma, d, V) <= SD_NOALLOC_SCRATCH_BYTES, else
  * SD_ESCRATCH before any GPU work (16 MiB holds, for example, 64 rows at V = 151936 or

@@ -63,18 +63,20 @@ def need_gpu():
 def test_noalloc_matches_workspace_call_twice_shrinking():
     # Calls in a row, each smaller than the one before: a tiled-regime problem (24
     # truncated requests), the greedy block of 9 at full size for 4 requests, a small
-    # truncating one, then a tiny one whose 16-workgroup contraction also decides (its
-    # last workgroup merges, using the scratch header's ticket word). Partials and
-    # drafted-token logits of earlier calls remain in the scratch and must not leak into
-    # later ones.
+    # truncating one, then two tiny ones whose contractions also decide (workgroups
+    # appended to their 16- and 8-workgroup grids merge partials published in the
+    # scratch's publication area, which each call must leave empty for the next).
+    # Partials and drafted-token logits of earlier calls remain in the scratch and must
+    # not leak into later ones.
     tiled = workload("ragged-b32", B=24, gamma=16, d=256, V=20000, T=0.0, name="noalloc-tiled")
     big = workload("greedy-block9", B=4, name="noalloc-big")
     small = workload("ragged-b32", B=3, gamma=16, d=512, V=3001, T=0.0, name="noalloc-small")
     tiny = workload("ragged-b32", B=2, gamma=4, d=256, V=1024, T=0.0, name="noalloc-tiny")
-    ws = (tiled, big, small, tiny)
+    tinier = workload("ragged-b32", B=1, gamma=4, d=256, V=512, T=0.0, name="noalloc-tinier")
+    ws = (tiled, big, small, tiny, tinier)
     sizes = [sd.verify_workspace_bytes(w.B, w.gamma, w.d, w.V) for w in ws]
-    assert sizes[0] > sizes[1] > sizes[2] > sizes[3] and sizes[0] <= sd.NOALLOC_SCRATCH_BYTES
-    for w, trunc in ((tiled, True), (big, False), (small, True), (tiny, True)):
+    assert all(a > b for a, b in zip(sizes, sizes[1:])) and sizes[0] <= sd.NOALLOC_SCRATCH_BYTES
+    for w, trunc in ((tiled, True), (big, False), (small, True), (tiny, True), (tinier, False)):
         say(w.name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} truncate={trunc}")
         acc = run_both(w, 0, trunc)
         say("accept_len", acc.tolist())
