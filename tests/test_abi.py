@@ -227,3 +227,17 @@ def test_verify_rejection_host_validation():
     assert _verify_rejection(wsv_bytes=100) == 4
     assert _verify_rejection(wsa=None) == 4
     assert _verify_rejection(wsa_bytes=100) == 4
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """No fallback: a copy of the package without libsdverify.so refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+    shutil.copytree(os.path.join(ROOT, "draft_block_verification_amd"),
+                    tmp_path / "draft_block_verification_amd",
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import draft_block_verification_amd"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "libsdverify.so is missing" in r.stderr
