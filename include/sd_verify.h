@@ -108,8 +108,8 @@ SD_API size_t sd_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t d, int
 SD_API size_t sd_accept_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
 
 /* Prepare a freshly allocated workspace: clears its 256-byte header (flag word and
- * counters) and, in a workspace of more than 256 + 2 * 525 KiB bytes (every verify
- * workspace), sets the publication area that follows the header to all ones bytes (the
+ * counters) and, in a workspace of at least 256 + 1049600 bytes (every verify workspace),
+ * sets the 1049600-byte publication area that follows the header to all ones bytes (the
  * state sd_verify_greedy's in-launch decision expects; every later call leaves it so).
  * Must be called once per workspace before its first use; enqueued on `stream`. */
 SD_API int32_t sd_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
