@@ -5,7 +5,7 @@ functions carry the C names and only marshal arguments; all computation runs
 in the library's HIP kernels.
 """
 from ._lib import (EXPORTED, FLAG_WAIT, FLAG_NO_RESIDUAL, FLAG_ROW_OFFSETS, FLAG_VERIFY_LEN, LIB_PATH,
-                   LM_HEAD_BLOCKED, LM_HEAD_ROWS, sd_verify_rejection,
+                   LM_HEAD_BLOCKED, LM_HEAD_ROWS, LM_HEAD_W12, sd_verify_rejection,
                    ROW_STATS_DTYPE, SCHED_EARLY_STOP, SCHED_MAX_CANDIDATES, SCHED_TOP_K, SdError,
                    BlockedWeights, VerifyRound, W12Weights, abi_version, accept_workspace_bytes, device_flags, new_stats,
                    new_workspace, profile_sps, sd_accept_greedy, sd_accept_rejection,
@@ -16,7 +16,7 @@ from ._lib import (EXPORTED, FLAG_WAIT, FLAG_NO_RESIDUAL, FLAG_ROW_OFFSETS, FLAG
                    w12_encode)
 
 __all__ = ["EXPORTED", "FLAG_WAIT", "FLAG_NO_RESIDUAL", "FLAG_ROW_OFFSETS", "FLAG_VERIFY_LEN", "LIB_PATH",
-           "LM_HEAD_BLOCKED", "LM_HEAD_ROWS", "sd_verify_rejection",
+           "LM_HEAD_BLOCKED", "LM_HEAD_ROWS", "LM_HEAD_W12", "sd_verify_rejection",
            "ROW_STATS_DTYPE", "SCHED_EARLY_STOP", "SCHED_MAX_CANDIDATES", "SCHED_TOP_K", "SdError",
            "BlockedWeights", "VerifyRound", "W12Weights", "abi_version", "accept_workspace_bytes", "device_flags", "new_stats",
            "new_workspace", "profile_sps", "sd_accept_greedy", "sd_accept_rejection",

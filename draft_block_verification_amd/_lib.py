@@ -79,7 +79,7 @@ ROW_STATS_DTYPE = np.dtype([("argmax", "<i4"), ("top1", "<f4"), ("top2", "<f4"),
 assert ROW_STATS_DTYPE.itemsize == 32
 
 FLAG_VERIFY_LEN, FLAG_ROW_OFFSETS, FLAG_NO_RESIDUAL, FLAG_WAIT = 1, 2, 4, 8
-LM_HEAD_ROWS, LM_HEAD_BLOCKED = 0, 1
+LM_HEAD_ROWS, LM_HEAD_BLOCKED, LM_HEAD_W12 = 0, 1, 2
 
 
 class SdError(RuntimeError):
@@ -580,20 +580,13 @@ def sd_verify_rejection(hidden: torch.Tensor, lm_head, draft_tokens: torch.Tenso
                         ws_verify: Optional[torch.Tensor] = None,
                         ws_accept: Optional[torch.Tensor] = None, stream=None):
     """Rejection verify in one call: returns (logits, stats, accept_len, next_token).
-    lm_head: bf16 [V][d] tensor or BlockedWeights; accept_rate float64 [B][gamma] or None
-    (not computed)."""
+    lm_head: bf16 [V][d] tensor, BlockedWeights or W12Weights; accept_rate float64
+    [B][gamma] or None (not computed)."""
     _need(hidden, "hidden", torch.bfloat16)
     B, g1, d = hidden.shape
     g = g1 - 1
-    if isinstance(lm_head, BlockedWeights):
-        if lm_head.d != d:
-            raise ValueError("lm_head must be [V][d] with the hidden size of `hidden`")
-        head, V, layout = _ptr(lm_head.buf), lm_head.V, LM_HEAD_BLOCKED
-    else:
-        head, V, fmt = _lm_head(lm_head, d)
-        if fmt:
-            raise ValueError("sd_verify_rejection reads a bf16 LM head or its blocked copy")
-        layout = LM_HEAD_ROWS
+    head, V, fmt = _lm_head(lm_head, d)
+    layout = {"": LM_HEAD_ROWS, "_blocked": LM_HEAD_BLOCKED, "_w12": LM_HEAD_W12}[fmt]
     dev = hidden.device
     _need(draft_tokens, "draft_tokens", torch.int32, (B, g))
     _need(draft_logits, "draft_logits", torch.bfloat16, (B, g, V))
@@ -638,8 +631,8 @@ class VerifyRound:
     truncate -> verify logits -> accept (greedy when temperature == 0, else rejection),
     all on one stream with no host synchronisation. The verify and accept steps run
     through sd_verify_greedy at temperature 0 and sd_verify_rejection otherwise (fewer
-    launches; a W12 LM head keeps the separate rejection calls); fused=False keeps the
-    separate sd_verify_logits + sd_accept_* calls.
+    launches, for every LM-head format); fused=False keeps the separate sd_verify_logits
+    + sd_accept_* calls.
     """
 
     def __init__(self, B: int, gamma: int, d: int, V: int, temperature: float,
@@ -685,7 +678,7 @@ class VerifyRound:
                              self.stats, self.accept_len, self.next_token, self.counters,
                              self.ws_verify, stream=stream)
             return self.accept_len, self.next_token
-        if self.T > 0 and self.fused and not isinstance(lm_head, W12Weights):
+        if self.T > 0 and self.fused:
             sd_verify_rejection(hidden, lm_head, draft_tokens, draft_logits, self.verify_len,
                                 self.row_offsets, u_accept, u_resample, self.T, self.logits,
                                 self.stats, self.accept_len, self.next_token, self.counters,

@@ -514,7 +514,7 @@ int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *stats,
 }
 
 
-int32_t sd_verify_rejection(const uint16_t *hidden, const uint16_t *lm_head,
+int32_t sd_verify_rejection(const uint16_t *hidden, const void *lm_head,
                             int32_t lm_head_layout, const uint16_t *draft_logits,
                             const int32_t *draft_tokens, const int32_t *verify_len,
                             const int32_t *row_offsets, const float *u_accept,
@@ -524,16 +524,20 @@ int32_t sd_verify_rejection(const uint16_t *hidden, const uint16_t *lm_head,
                             double *accept_rate, void *verify_workspace,
                             size_t verify_workspace_bytes, void *accept_workspace,
                             size_t accept_workspace_bytes, void *stream) {
-  if (lm_head_layout != SD_LM_HEAD_ROWS && lm_head_layout != SD_LM_HEAD_BLOCKED) return SD_EINVAL;
-  if (!logits || !stats || !draft_logits || !draft_tokens || !u_accept || !u_resample ||
-      !accept_len || !next_token)
+  if (lm_head_layout != SD_LM_HEAD_ROWS && lm_head_layout != SD_LM_HEAD_BLOCKED &&
+      lm_head_layout != SD_LM_HEAD_W12)
+    return SD_EINVAL;
+  if (!lm_head || !logits || !stats || !draft_logits || !draft_tokens || !u_accept ||
+      !u_resample || !accept_len || !next_token)
     return SD_EINVAL;
   if (!isfinite(temperature) || !(temperature > 0.f)) return SD_EINVAL;
+  const bool w12 = lm_head_layout == SD_LM_HEAD_W12;
   VerifyArgs a;
-  const int32_t st = verify_setup(hidden, lm_head, nullptr, lm_head_layout == SD_LM_HEAD_BLOCKED,
-                                  draft_tokens, verify_len, row_offsets, B, gamma, d, V,
-                                  temperature, logits, stats, true, verify_workspace,
-                                  verify_workspace_bytes, &a);
+  const int32_t st = verify_setup(
+      hidden, w12 ? nullptr : static_cast<const uint16_t *>(lm_head),
+      w12 ? static_cast<const sd_w12 *>(lm_head) : nullptr, lm_head_layout == SD_LM_HEAD_BLOCKED,
+      draft_tokens, verify_len, row_offsets, B, gamma, d, V, temperature, logits, stats, true,
+      verify_workspace, verify_workspace_bytes, &a);
   if (st != SD_OK) return st;
   if (!aligned(draft_logits, 16) || !aligned(u_accept, 4) || !aligned(u_resample, 4) ||
       !aligned(accept_len, 4) || !aligned(next_token, 4) || (counters && !aligned(counters, 8)) ||

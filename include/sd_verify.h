@@ -443,7 +443,8 @@ SD_API int32_t sd_accept_rejection_ex(const float *logits, const sd_row_stats *s
 /* LM-head layouts of sd_verify_rejection. */
 enum {
     SD_LM_HEAD_ROWS = 0,     /* bf16 [V][d]                                              */
-    SD_LM_HEAD_BLOCKED = 1   /* the stage-major blocked copy written by sd_lm_head_block */
+    SD_LM_HEAD_BLOCKED = 1,  /* the stage-major blocked copy written by sd_lm_head_block */
+    SD_LM_HEAD_W12 = 2       /* lm_head points to an sd_w12 descriptor (host memory)     */
 };
 
 /*
@@ -457,8 +458,10 @@ enum {
  * the GPU has workgroup slots its grid leaves idle.
  *   hidden, draft_tokens, verify_len, row_offsets, B, gamma, d, V
  *                as for sd_verify_logits (draft_tokens required)
- *   lm_head      bf16 [V][d] (lm_head_layout SD_LM_HEAD_ROWS) or its blocked copy
- *                (SD_LM_HEAD_BLOCKED, streaming regime only, else SD_ESHAPE)
+ *   lm_head      bf16 [V][d] (lm_head_layout SD_LM_HEAD_ROWS), its blocked copy
+ *                (SD_LM_HEAD_BLOCKED), or a host sd_w12 descriptor of the W12 stream
+ *                (SD_LM_HEAD_W12, checked as for sd_verify_logits_w12); the last two in
+ *                the streaming regime only, else SD_ESHAPE
  *   draft_logits, u_accept, u_resample, temperature (> 0)
  *                as for sd_accept_rejection
  *   logits, stats  out, as for sd_verify_logits (both required)
@@ -473,7 +476,7 @@ enum {
  * Errors: those of sd_verify_logits and sd_accept_rejection_ex; SD_EINVAL for an unknown
  * lm_head_layout.
  */
-SD_API int32_t sd_verify_rejection(const uint16_t *hidden, const uint16_t *lm_head,
+SD_API int32_t sd_verify_rejection(const uint16_t *hidden, const void *lm_head,
                                    int32_t lm_head_layout, const uint16_t *draft_logits,
                                    const int32_t *draft_tokens, const int32_t *verify_len,
                                    const int32_t *row_offsets, const float *u_accept,

@@ -213,7 +213,8 @@ def _verify_rejection(**kw):
 
 
 def test_verify_rejection_host_validation():
-    assert _verify_rejection(layout=2) == 1            # unknown LM-head layout
+    assert _verify_rejection(layout=3) == 1            # unknown LM-head layout
+    assert _verify_rejection(lm_head=None) == 1
     assert _verify_rejection(logits=None) == 1         # the draws need the logits
     assert _verify_rejection(dlog=None) == 1
     assert _verify_rejection(ur=None) == 1
@@ -227,6 +228,16 @@ def test_verify_rejection_host_validation():
     assert _verify_rejection(wsv_bytes=100) == 4
     assert _verify_rejection(wsa=None) == 4
     assert _verify_rejection(wsa_bytes=100) == 4
+    # A W12 head: a host descriptor, checked as for sd_verify_logits_w12.
+    from draft_block_verification_amd._lib import _SdW12
+    desc = lambda **f: ctypes.byref(_SdW12(**dict(dict(codes=0x10000, corr=0x10000, cap=12, b2=5), **f)))
+    assert _verify_rejection(layout=2, lm_head=desc(codes=None)) == 1
+    assert _verify_rejection(layout=2, lm_head=desc(b2=0)) == 1
+    assert _verify_rejection(layout=2, lm_head=desc(), d=200) == 2   # streaming regime only
+    assert _verify_rejection(layout=2, lm_head=desc(), B=16) == 2
+    assert _verify_rejection(layout=2, lm_head=desc(cap=6)) == 2     # cap % 4 == 0
+    assert _verify_rejection(layout=2, lm_head=desc(codes=0x10008)) == 3
+    assert _verify_rejection(layout=2, lm_head=desc(), wsv_bytes=100) == 4
 
 
 def test_import_fails_loudly_without_the_library(tmp_path):

@@ -305,6 +305,10 @@ REJ_FUSED = [
     ("rej-gamma64", dict(B=2, gamma=64, d=64, V=4099, truncate=False)),
     ("rej-many", dict(B=300, gamma=3, d=64, V=129, truncate=True)),
     ("rej-blocked", dict(B=3, gamma=16, d=256, V=9000, truncate=True, blocked=True)),
+    # The W12 stream (decoded in the streaming contraction), with appended drafter
+    # workgroups and on a full grid.
+    ("rej-w12", dict(B=3, gamma=16, d=256, V=9000, truncate=True, w12=True)),
+    ("rej-w12-full-grid", dict(B=1, gamma=9, d=256, V=65536, truncate=False, w12=True)),
 ]
 
 
@@ -317,11 +321,14 @@ def test_fused_rejection_matches_separate_calls(case):
     name, over = case
     over = dict(over)
     blocked = over.pop("blocked", False)
+    w12 = over.pop("w12", False)
     w = workload("ragged-b32", T=0.9, geo_p=(0.2,), name=name, **over)
     W = make_weights(w)
     W_dev = bf16_dev(W)
     if blocked:
         W_dev = sd.BlockedWeights(W_dev)
+    if w12:
+        W_dev = sd.W12Weights.from_bf16(W)
     for step in range(2):
         say(name, f"B={w.B} g={w.gamma} d={w.d} V={w.V} T={w.T} step={step}")
         ds = upload_step(make_step(w, W, step))
