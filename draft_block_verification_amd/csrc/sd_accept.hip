@@ -678,55 +678,66 @@ __global__ __launch_bounds__(256) void k_draw_finalize(RejArgs a) {
 }
 
 // The draw in one launch, for grids whose workgroups the chip holds all at once (C <=
-// kDrawOnePassMaxChunks and B * C no more than the resident workgroups):
-// workgroup (c, r) forms the weights of its chunk's ids (kPer consecutive ids per thread)
-// for both the residual (or bonus) column and p, sums them, and publishes the two sums
-// with device-scope atomic stores into slots the decision kernel set to kUnpublished.
-// Each workgroup then waits for all C sums of its request, locates the draw exactly as
-// k_draw_finalize does, and the workgroup holding the hit chunk finishes the draw from
-// the weights still in its registers. The wait is bounded: a workgroup that has polled a
-// slot kDrawSpinLimit times raises SD_FLAG_WAIT and writes -1, and the request's
-// token is then not valid.
+// kDrawOnePassMaxChunks and B * ceil(C / K) no more than the resident workgroups):
+// workgroup (g, r) takes chunks gK .. gK + K - 1 of request r in turn, forms the weights
+// of each chunk's ids (kPer consecutive ids per thread) for both the residual (or bonus)
+// column and p, sums them, and publishes the two sums with device-scope atomic stores
+// into slots the decision kernel set to kUnpublished. Each workgroup then waits for all C
+// sums of its request, locates the draw exactly as k_draw_finalize does, and the
+// workgroup holding the hit chunk finishes the draw from that chunk's weights (still in
+// its registers when it is the last chunk it formed, else formed again by the same code,
+// so the same bits). The wait is bounded: a workgroup that has polled a slot
+// kDrawSpinLimit times raises SD_FLAG_WAIT and writes -1, and the request's token is
+// then not valid.
 constexpr int kDrawOnePassMaxChunks = 256;
+constexpr int kDrawOnePassMaxPerGroup = 8;
 constexpr int kDrawSpinLimit = 1 << 20;
 __device__ inline unsigned long long published_bits(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
   return b == kUnpublished ? 0x7ff8000000000000ull : b;   // never the empty-slot pattern
 }
 
-__global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a) {
-  __shared__ double s_d[8];
-  __shared__ int s_i[12];
-  __shared__ double s_cs[2 * kDrawOnePassMaxChunks];
-  __shared__ int s_late;
-  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  DrawRow d;
-  int arow, acc;
-  if (!draw_row(a, r, &d, &arow, &acc)) return;
-  const int v0 = c * kChunk + tid * kPer;
-  float wp[kPer], wr[kPer];
-  {
-    DrawRow dp = d;
-    dp.q = nullptr;
-    draw_thread_weights(a, dp, v0, wp);
-  }
+// Weights of chunk c of request r's draw row: wp from p, wr from the residual (or p).
+__device__ inline void draw_chunk_weights(const RejArgs &a, const DrawRow &d, int c,
+                                          float (&wp)[kPer], float (&wr)[kPer]) {
+  const int v0 = c * kChunk + threadIdx.x * kPer;
+  DrawRow dp = d;
+  dp.q = nullptr;
+  draw_thread_weights(a, dp, v0, wp);
   if (d.q) {
     draw_thread_residual(a, d, v0, wp, wr);
   } else {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) wr[e] = wp[e];
   }
-  double sr = 0.0, sp = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) { sr += (double)wr[e]; sp += (double)wp[e]; }
-  sr = block_sum_d(sr, s_d);
-  sp = block_sum_d(sp, s_d);
+}
+
+__global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a, int K) {
+  __shared__ double s_d[8];
+  __shared__ int s_i[12];
+  __shared__ double s_cs[2 * kDrawOnePassMaxChunks];
+  __shared__ int s_late;
+  const int cg = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  DrawRow d;
+  int arow, acc;
+  if (!draw_row(a, r, &d, &arow, &acc)) return;
   unsigned long long *pub = reinterpret_cast<unsigned long long *>(a.csum) + (size_t)r * a.C * 2;
-  if (tid == 0) {
-    __hip_atomic_store(pub + 2 * c, published_bits(sr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pub + 2 * c + 1, published_bits(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_late = 0;
+  float wp[kPer], wr[kPer];
+  int last = -1;
+  for (int c = cg * K; c < min(cg * K + K, a.C); ++c) {
+    draw_chunk_weights(a, d, c, wp, wr);
+    last = c;
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) { sr += (double)wr[e]; sp += (double)wp[e]; }
+    sr = block_sum_d(sr, s_d);
+    sp = block_sum_d(sp, s_d);
+    if (tid == 0) {
+      __hip_atomic_store(pub + 2 * c, published_bits(sr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pub + 2 * c + 1, published_bits(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  if (tid == 0) s_late = 0;
   __syncthreads();
   for (int k = tid; k < 2 * a.C; k += 256) {
     unsigned long long v = kUnpublished;
@@ -748,15 +759,16 @@ __global__ __launch_bounds__(256) void k_draw_onepass(RejArgs a) {
   }
   const DrawLoc loc = draw_locate(a, r, acc, d.q != nullptr, s_cs, s_d, s_i);
   if (loc.hit < 0) {
-    if (c == 0 && tid == 0) a.next_token[r] = a.stats[arow].argmax;
+    if (cg == 0 && tid == 0) a.next_token[r] = a.stats[arow].argmax;
     return;
   }
-  if (loc.hit != c) return;
+  if (loc.hit / K != cg) return;
+  if (loc.hit != last) draw_chunk_weights(a, d, loc.hit, wp, wr);
   if (loc.col == 1) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) wr[e] = wp[e];
   }
-  draw_in_chunk(a, r, wr, v0, loc, s_d, s_i);
+  draw_in_chunk(a, r, wr, loc.hit * kChunk + tid * kPer, loc, s_d, s_i);
 }
 
 // Second grid dimension for a row range (the hardware bounds it at 65535).
@@ -910,9 +922,13 @@ hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const fl
   // The draw in one launch when the chip holds all of its workgroups at once (each then
   // runs to its wait, so the wait ends even beside other work) and no acceptance rates
   // ride along.
-  const bool onepass_draw =
-      one_pass && !accept_rate && a.C <= kDrawOnePassMaxChunks &&
-      (long long)v.rm.B * a.C <= resident_workgroups(reinterpret_cast<const void *>(&k_draw_onepass));
+  // Chunks per workgroup: the fewest that let the chip hold the whole grid, at most
+  // kDrawOnePassMaxPerGroup.
+  const long long resident = resident_workgroups(reinterpret_cast<const void *>(&k_draw_onepass));
+  int K = 1;
+  while (K < kDrawOnePassMaxPerGroup && (long long)v.rm.B * ((a.C + K - 1) / K) > resident) ++K;
+  const bool onepass_draw = one_pass && !accept_rate && a.C <= kDrawOnePassMaxChunks &&
+                            (long long)v.rm.B * ((a.C + K - 1) / K) <= resident;
   if (one_pass) {
     DecideArgs o{u_accept, a.lse_q, a.rec, accept_len, next_token, counters,
                  onepass_draw ? reinterpret_cast<unsigned long long *>(a.csum) : nullptr, a.C};
@@ -923,7 +939,7 @@ hipError_t launch_verify_rejection(VerifyArgs v, const float *u_accept, const fl
   }
   if (e != hipSuccess) return e;
   if (onepass_draw) {
-    hipLaunchKernelGGL(k_draw_onepass, dim3(a.C, v.rm.B), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_draw_onepass, dim3((a.C + K - 1) / K, v.rm.B), dim3(256), 0, stream, a, K);
     return hipGetLastError();
   }
   return launch_draws(a, stream);

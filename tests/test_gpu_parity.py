@@ -97,6 +97,9 @@ SHAPES = [
     # first one that falls back to two launches.
     ("vocab-256-chunks-rej", 1, 2, 8, 1048000, 1.0, False),
     ("vocab-269-chunks-rej", 1, 2, 8, 1100000, 0.8, False),
+    # 64 requests x 35 chunks: more draw workgroups than the chip holds, so the one-launch
+    # draw takes two chunks per workgroup.
+    ("draw-2-chunks-per-group-rej", 64, 1, 64, 140000, 1.0, False),
 ]
 
 
@@ -309,6 +312,8 @@ REJ_FUSED = [
     # workgroups and on a full grid.
     ("rej-w12", dict(B=3, gamma=16, d=256, V=9000, truncate=True, w12=True)),
     ("rej-w12-full-grid", dict(B=1, gamma=9, d=256, V=65536, truncate=False, w12=True)),
+    # A one-launch draw with two chunks per workgroup (64 requests x 35 chunks).
+    ("rej-draw-2-chunks-per-group", dict(B=64, gamma=1, d=64, V=140000, truncate=False)),
 ]
 
 
